@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""SFA benchmark on one MI355X.
+
+Headline step: the long-context 7B-shaped prefill -- batch 1, 65,536 tokens,
+28 query / 4 KV heads, head_dim 128, bf16 in and out, window 16, γ 0.98,
+α 0.1 -- over 28 stacked layers, each layer with its own seeded inputs (one
+call of sfa_prefill per layer, run back to back; the inputs are resident in HBM
+before timing starts).  A step is the 28 calls; value = tokens·heads/s =
+65,536 · 28 heads · 28 layers / step time.
+
+The roofline object covers the dominant kernel, the windowed-attention pass
+(SFA_PREFILL_ATTEND): its average duration comes from HIP events recorded on
+the launch stream around that part of every call in the timed region, and its
+algorithmic bytes are one read of Q, K, V, one write of O and the ring
+hand-off.  The EWMA scan part (SFA_PREFILL_SCAN) runs just before it in every
+call and is part of the step time.
+
+Also reported in the same line: the 28-layer batched decode step (256
+sequences) and the 24-layer triple-channel enhancement, each with its own
+achieved HBM bandwidth, and the CPU fp64 oracle timed on this host.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import windowed_ewma_state_amd as sfa  # noqa: E402
+from windowed_ewma_state_amd import _lib, inputs  # noqa: E402
+
+PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+METRIC = "SFA tokens·heads/s (prefill, decode) + achieved HBM GB/s vs MI355X peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_window_attn_prefill_7b_64k_traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "windowed_ewma_state_amd", "csrc", "prefill.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# prefill, 7B-shaped, 64K tokens, stacked layers
+# ----------------------------------------------------------------------------
+B, N, HQ, HKV, HD, WIN = 1, 65536, 28, 4, 128, 16
+
+
+def prefill_bytes_per_launch():
+    """Algorithmic HBM bytes of one attention pass: Q, K, V read once, O written
+    once (bf16), plus the ring hand-off (last W keys/values)."""
+    q = B * N * HQ * HD * 2
+    kv = 2 * B * N * HKV * HD * 2
+    o = B * N * HQ * HD * 2
+    ring = 2 * B * HKV * WIN * HD * 2
+    return q + kv + o + ring
+
+
+def run_prefill(args):
+    dev = torch.device("cuda:0")
+    L = args.layers
+    log(f"prefill: generating {L} layers of seeded inputs on the GPU")
+    layers = []
+    for l in range(L):
+        d = inputs.workload(4, device=dev, layer=l)
+        layers.append(dict(
+            q=d["q"], k=d["k"], v=d["v"], gamma=d["gamma"], alpha=d["alpha"],
+            out=torch.empty((B, N, HQ, HD), dtype=torch.bfloat16, device=dev),
+            ring_k=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
+            ring_v=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
+            state=torch.zeros((B, HKV, HD), dtype=torch.float32, device=dev)))
+    ws = torch.empty(sfa.prefill_workspace_size(B, N, HKV, HD), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        for l, x in enumerate(layers):
+            kw = dict(window=WIN, out=x["out"], ring_k=x["ring_k"], ring_v=x["ring_v"],
+                      state=x["state"], workspace=ws, stream=stream)
+            sfa.prefill(x["q"], x["k"], x["v"], x["gamma"], x["alpha"], parts=_lib.SFA_PREFILL_SCAN, **kw)
+            if evs is not None:
+                evs[l][0].record(stream)
+            sfa.prefill(x["q"], x["k"], x["v"], x["gamma"], x["alpha"], parts=_lib.SFA_PREFILL_ATTEND, **kw)
+            if evs is not None:
+                evs[l][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(L)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    return dict(layers=layers, wall=wall, attn_ms=sum(attn_ms) / len(attn_ms))
+
+
+# ----------------------------------------------------------------------------
+# secondary: decode step (28 layers x 256 sequences) and enhancement (24 layers)
+# ----------------------------------------------------------------------------
+def decode_bytes(L=28, Bd=256, Hq=28, Hkv=4, d=128, W=16):
+    """Per step: q, k_new, v_new, 16 ring keys + 15 ring values (the evicted
+    value is never read), one ring slot written (K and V), S read and written
+    (fp32), O written (bf16), pos."""
+    per = (Hq * d * 2 + 2 * Hkv * d * 2 + Hkv * W * d * 2 + Hkv * (W - 1) * d * 2
+           + 2 * Hkv * d * 2 + 2 * Hkv * d * 4 + Hq * d * 2)
+    return L * Bd * per + Bd * 4
+
+
+def run_decode(steps=40, warmup=5, sets=3):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    bufs = []
+    for i in range(sets):  # rotate input sets so the 256 MB MALL cannot hold them
+        d = inputs.workload(3, device=dev) if i == 0 else inputs.decode_inputs(
+            28, 256, 28, 4, 128, seed=2000 + i, device=dev)
+        d["out"] = torch.empty((28, 256, 28, 128), dtype=torch.bfloat16, device=dev)
+        bufs.append(d)
+
+    def call(d):
+        sfa.decode_step(d["q"], d["k_new"], d["v_new"], d["ring_k"], d["ring_v"], d["state"], d["pos"],
+                        d["gamma"], d["alpha"], out=d["out"], stream=stream)
+
+    for i in range(warmup):
+        call(bufs[i % sets])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(bufs[i % sets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    byts = decode_bytes()
+    return {"workload": "7B-shaped decode step, 28 layers x 256 sequences, 28/4 heads, d 128, bf16",
+            "value": 28 * 256 * 28 / (ms * 1e-3), "unit": "tokens·heads/s (sequence, query head, layer)",
+            "us_per_step": ms * 1e3, "kernel": "k_decode",
+            "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": byts}}
+
+
+def enhance_bytes(L=24, T=4096, H=1024, S=64, R=16):
+    return L * T * H * 2 * 2 + L * S * H * 4 + 2 * L * R * H * 4 + 2 * L * H * 4
+
+
+def run_enhance(steps=20, warmup=3, sets=3):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    L, T, H = 24, 4096, 1024
+    bufs = []
+    for i in range(sets):
+        d = inputs.workload(5, device=dev) if i == 0 else inputs.enhance_inputs(L, T, H, seed=3000 + i,
+                                                                                device=dev)
+        d["ring"] = torch.zeros((L, 16, H), device=dev)
+        d["field"] = torch.zeros((L, H), device=dev)
+        d["out"] = torch.empty((L, T, H), dtype=torch.bfloat16, device=dev)
+        bufs.append(d)
+    ws = torch.empty(sfa.enhance_workspace_size(L, T, H), dtype=torch.uint8, device=dev)
+
+    def call(d):
+        sfa.enhance(d["attn"], d["pool"], d["ring"], d["field"], out=d["out"], workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        call(bufs[i % sets])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(bufs[i % sets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    byts = enhance_bytes()
+    return {"workload": "triple-channel enhancement, 24 layers x 4096 tokens, hidden 1024, 64 slots, bf16",
+            "value": L * T / (ms * 1e-3), "unit": "tokens·layers/s", "us_per_call": ms * 1e3,
+            "kernel": "sfa_enhance (5 launches)",
+            "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_call": byts}}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on whole layers of the same workload
+# ----------------------------------------------------------------------------
+def cpu_baseline(n_layers, budget_s=10.0):
+    import numpy as np
+
+    import oracle
+    done, t_cpu = 0, 0.0
+    for l in range(n_layers):
+        x = inputs.workload(4, device="cuda", layer=l)  # the same seeded inputs as the GPU run
+        q = np.ascontiguousarray(x["q"].float().cpu().numpy())
+        k = np.ascontiguousarray(x["k"].float().cpu().numpy())
+        v = np.ascontiguousarray(x["v"].float().cpu().numpy())
+        g, a = x["gamma"].cpu(), x["alpha"].cpu()
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, g, a, WIN)
+        t_cpu += time.perf_counter() - t0
+        done += 1
+        log(f"cpu baseline: oracle layer {done} done, {t_cpu:.1f} s")
+        if t_cpu >= budget_s:
+            break
+    return {"value": done * B * N * HQ / t_cpu, "unit": "tokens·heads/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": t_cpu,
+            "sample": f"{done} of the 28 layers of the same 64K-token prefill workload, fp64 C oracle "
+                      f"(OpenMP over heads), wall time of the oracle call only"}
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("prefill_src_sha256_16") != src_hash(PREFILL_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=28, help="stacked prefill layers per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every kernel here runs on a single MI355X "
+              "(see the sharding notes in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    pre = run_prefill(args)
+    ms_step = pre["wall"] * 1e3 / args.steps
+    value = B * N * HQ * args.layers / (pre["wall"] / args.steps)
+    byts = prefill_bytes_per_launch()
+    achieved = byts / (pre["attn_ms"] * 1e-3)
+    tr = traffic()
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens·heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "7B-shaped long-context SFA prefill, 28 stacked layers",
+                   "batch": B, "seq_len": N, "q_heads": HQ, "kv_heads": HKV, "head_dim": HD,
+                   "window": WIN, "layers": args.layers, "gamma": 0.98, "alpha": 0.1},
+        "roofline": {"bound": "hbm", "kernel": "k_window_attn", "achieved": achieved / 1e9,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": achieved / PEAK_HBM,
+                     "traffic": tr, "algorithmic_bytes_per_launch": byts,
+                     "avg_launch_us": pre["attn_ms"] * 1e3},
+        "prefill_step_gbps": byts * args.layers / (ms_step * 1e-3) / 1e9,
+    }
+    del pre["layers"]
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        res["decode"] = run_decode()
+        res["enhance"] = run_enhance()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.layers)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * sfa.h -- C ABI of the MI355X (gfx950) Signal Field Attention library, libsfa.so.
+ *
+ * Signal Field Attention (SFA) is a dual-channel attention:
+ *   near field  O_near = softmax(q_t · K_near^T / sqrt(d)) · V_near over the most
+ *               recent W (= k = 16) tokens, the current one included;
+ *   far field   S_t = γ·S_{t-1} + (1-γ)·k_evicted, where k_evicted is the key that
+ *               leaves the window at step t (the key of position t-W);
+ *   fusion      O = O_near + α·S_t.
+ * Source: page "Signal Field Attention (SFA)：8KB代码实现4.16倍推理加速与248倍内存压缩",
+ * section 2.1 (near-field, far-field and fusion equations) and section 2.2
+ * (k = 16, constant O(k·d) memory).  The optional triple-channel enhancement
+ * follows page "Dalin Soma SFA基于信号场注意力机制的神经网络推理加速框架"
+ * sections 2.1-2.2 and the SFA_Config defaults of page "Signal Field Attention
+ * (SFA)" (project README).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees, copies to the host or synchronises.  Work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and is
+ *    asynchronous: results are valid once the stream reaches that point.
+ *  - Layouts are dense and row-major.  "BNHD" = [batch, tokens, heads, head_dim]
+ *    (the layout a fused QKV projection emits).
+ *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *  - S (the far-field state) is one fp32 d-vector per KV head; γ is per KV head,
+ *    α per query head.
+ *  - Ring cache: W slots per (layer, sequence, KV head); the key/value of
+ *    position p lives in slot p mod W.
+ *  - dtype codes: SFA_F32 (IEEE fp32) or SFA_BF16 (bfloat16).  in_dtype applies
+ *    to q/k/v, the ring and the attention input; out_dtype to the outputs.
+ *    Arithmetic is fp32 (bf16 MFMA products with fp32 accumulation, exact for
+ *    bf16 operands; fp32 inputs use fp32 MFMA).
+ *  - Errors: arguments are validated before anything is enqueued.  A NULL
+ *    required pointer, a negative or inconsistent size, Hq % Hkv != 0,
+ *    window outside [1,16] or a too-small workspace returns
+ *    SFA_ERR_INVALID_ARG; head_dim other than 64/128 or an unknown dtype
+ *    returns SFA_ERR_UNSUPPORTED; a failed kernel launch returns SFA_ERR_HIP.
+ *    On any error nothing has been written.  Zero-sized work (n == 0, B == 0,
+ *    T == 0, L == 0) returns SFA_OK and enqueues nothing.
+ *  - Thread safety: no global mutable state.  Concurrent calls are safe as long
+ *    as they do not share output, state or workspace buffers.
+ */
+#ifndef SFA_H
+#define SFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SFA_OK = 0,
+    SFA_ERR_INVALID_ARG = 1,
+    SFA_ERR_UNSUPPORTED = 2,
+    SFA_ERR_HIP = 3
+};
+
+enum { SFA_F32 = 0, SFA_BF16 = 1 };
+
+/* Largest window (ring slots) supported: the k = 16 of the near field. */
+#define SFA_MAX_WINDOW 16
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *sfa_status_string(int status);
+
+/* Library ABI version (incremented on any signature change). */
+int sfa_abi_version(void);
+
+/*
+ * Workspace bytes sfa_prefill needs for (B, n, Hkv, d): the chunked EWMA scan
+ * keeps fp32 per-chunk aggregates and carries, proportional to B·Hkv·ceil(n/64)·d.
+ * Returns 0 for zero-sized work.  Alignment of the workspace: 256 bytes.
+ */
+size_t sfa_prefill_workspace_size(int B, int n, int Hkv, int d);
+
+/*
+ * sfa_prefill -- near-field windowed attention + far-field EWMA over a prompt.
+ * (Near-field, far-field and fusion equations of the first page, section 2.1.)
+ *
+ * For every batch b, query head h (KV head G = h / (Hq/Hkv)) and token t with
+ * position p = p0[b] + t (p0 = pos0[b], or 0 when pos0 is NULL):
+ *   if p >= W:  S <- γ[G]·S + (1-γ[G])·key(p-W)         (the key leaving the window)
+ *   O[b,t,h] = Σ_{j=max(0,p-W+1)}^{p} softmax_j(scale·<q, key(j)>)·value(j) + α[h]·S
+ * S starts at 0 for a fresh sequence (pos0 NULL or pos0[b] == 0) and at
+ * state[b,G] otherwise.  key/value(j) for j < p0 come from the ring.
+ *
+ *  q        [B,n,Hq,d]  in_dtype, BNHD.
+ *  k, v     [B,n,Hkv,d] in_dtype, BNHD.
+ *  gamma    [Hkv] fp32, decay of each KV head's far field, in [0,1].
+ *  alpha    [Hq]  fp32, far-field mixing coefficient of each query head.
+ *  out      [B,n,Hq,d]  out_dtype (written).
+ *  ring_k, ring_v [B,Hkv,W,d] in_dtype.  On return slot p mod W holds the
+ *           key/value of position p for the last min(W, p0+n) positions;
+ *           slots of older positions are left untouched.  With pos0 != NULL
+ *           they are also read (positions p0-W..p0-1).  May both be NULL only
+ *           when pos0 is NULL (then the ring is not produced).
+ *  state    [B,Hkv,d] fp32: S after the last token (written).  With
+ *           pos0 != NULL it is read first as the carried S.  May be NULL
+ *           only when pos0 is NULL.
+ *  pos0     [B] int32 device array or NULL: position of each sequence's first
+ *           token in this call (chunked prefill / continuation).  Read-only;
+ *           negative entries are treated as 0.
+ *  window   W in [1,16]; scale <= 0 selects 1/sqrt(d).
+ *  workspace, workspace_bytes: device scratch of at least
+ *           sfa_prefill_workspace_size(B, n, Hkv, d) bytes, 256-byte aligned.
+ */
+int sfa_prefill(const void *q, const void *k, const void *v,
+                const float *gamma, const float *alpha,
+                void *out, void *ring_k, void *ring_v, float *state,
+                const int32_t *pos0,
+                int B, int n, int Hq, int Hkv, int d, int window, float scale,
+                int in_dtype, int out_dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sfa_prefill_part -- the two phases of sfa_prefill, for callers that schedule
+ * or time them separately (same arguments as sfa_prefill, plus `parts`).
+ *   SFA_PREFILL_SCAN    far-field EWMA scan: per-chunk aggregates and the S
+ *                       carried into every 64-token chunk (into the
+ *                       workspace), and the final S into `state`.
+ *   SFA_PREFILL_ATTEND  windowed attention + α·S epilogue for every token
+ *                       (reads the carries from the workspace), and the ring
+ *                       hand-off.  Must run after SCAN with the same arguments
+ *                       and workspace, on the same stream (or ordered after it).
+ * parts = SCAN | ATTEND is exactly sfa_prefill.  Other values of `parts`
+ * return SFA_ERR_INVALID_ARG.
+ */
+enum { SFA_PREFILL_SCAN = 1, SFA_PREFILL_ATTEND = 2 };
+int sfa_prefill_part(int parts, const void *q, const void *k, const void *v,
+                     const float *gamma, const float *alpha,
+                     void *out, void *ring_k, void *ring_v, float *state,
+                     const int32_t *pos0,
+                     int B, int n, int Hq, int Hkv, int d, int window, float scale,
+                     int in_dtype, int out_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sfa_decode_step -- one generated token for L layers at once.
+ * (First page, section 2.1 equations with the constant-memory k-slot ring of
+ * section 2.2.)
+ *
+ * For each layer l, sequence b and KV head G, with p = pos[b] and s = p mod W:
+ *   if p >= W:  S <- γ[l,G]·S + (1-γ[l,G])·ring_k[s]   (old contents: position p-W)
+ *   ring_k[s] <- k_new;  ring_v[s] <- v_new
+ *   for each query head h of the group: softmax over the valid slots (all W
+ *   when p >= W-1, else slots 0..p), O = Σ p_j·ring_v[j] + α[l,h]·S.
+ * The result equals token p of a prefill of the whole sequence.
+ *
+ *  q            [L,B,Hq,d]  in_dtype.
+ *  k_new, v_new [L,B,Hkv,d] in_dtype.
+ *  ring_k, ring_v [L,B,Hkv,W,d] in_dtype, updated in place (only slot s).
+ *  state        [L,B,Hkv,d] fp32, updated in place.
+ *  pos          [B] int32, >= 0, read-only; the caller advances it once per
+ *               step (so one launch can cover all L layers without a race).
+ *               A sequence with a negative entry is skipped (nothing written).
+ *  gamma        [L,Hkv] fp32;  alpha [L,Hq] fp32.
+ *  out          [L,B,Hq,d] out_dtype (written).
+ */
+int sfa_decode_step(const void *q, const void *k_new, const void *v_new,
+                    void *ring_k, void *ring_v, float *state,
+                    const int32_t *pos, const float *gamma, const float *alpha,
+                    void *out, int L, int B, int Hq, int Hkv, int d, int window,
+                    float scale, int in_dtype, int out_dtype, void *stream);
+
+/*
+ * Workspace bytes sfa_enhance needs for (L, T, H): per-chunk fp32 aggregates
+ * of the EMA field, proportional to L·ceil(T/64)·H.  256-byte aligned.
+ */
+size_t sfa_enhance_workspace_size(int L, int T, int H);
+
+/*
+ * sfa_enhance -- optional triple-channel enhancement applied to an attention
+ * output.  (Page "Dalin Soma SFA..." section 2.1: ring-buffer channel, EMA
+ * field channel, 64-slot semantic pool; section 2.2: fusion, clip and the
+ * per-layer factor; section 2.4: the ring mean always divides by the ring
+ * size.  Defaults from the SFA_Config of page "Signal Field Attention (SFA)".)
+ *
+ * For layer i (global index lg = layer0 + i) and token t (global index t0 + t),
+ * with a = attn[i,t,:] (H = hidden size, the whole row; no per-head split):
+ *   ring[(t0+t) mod R] <- a;  rm = Σ ring / R
+ *   field <- γ_e·field + (1-γ_e)·a
+ *   c_j = <a, s_j> / (max(|a|,1e-12)·max(|s_j|,1e-12)),  w = softmax(c / T),
+ *   sem = Σ_j w_j·s_j
+ *   e = rm + 0.5·field + 0.5·sem
+ *   enh = α_lg·clip(e, -clip, +clip),  out = a + enh
+ *   α_lg = α_base·(0.3 + 0.7·lg/(n_layers-1))·cross_decay^lg  (ratio 0 if n_layers == 1)
+ *
+ *  attn         [L,T,H] in_dtype.
+ *  out          [L,T,H] out_dtype (written; may not alias attn).
+ *  ring         [L,R,H] fp32, carried ring (zeros for a fresh stream), updated.
+ *  field        [L,H] fp32, carried field (zeros for a fresh stream), updated.
+ *  pool         fp32 slots of layer i at pool + i·pool_layer_stride, each
+ *               [n_slots,H]; pool_layer_stride = 0 shares one pool.  Read-only.
+ *  enhancement  [L,T,H] fp32 or NULL: enh values (written when non-NULL).
+ *  R = ring_size in [1,16]; n_slots in [1,64]; temperature > 0; clip >= 0.
+ *  workspace:   at least sfa_enhance_workspace_size(L, T, H) bytes.
+ */
+int sfa_enhance(const void *attn, void *out, float *ring, float *field,
+                const float *pool, long long pool_layer_stride, float *enhancement,
+                int L, int layer0, int n_layers, int T, int H, int t0,
+                float alpha_base, float cross_decay, float ema_gamma, float temperature,
+                float clip, int ring_size, int n_slots,
+                int in_dtype, int out_dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFA_H */

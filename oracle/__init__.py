@@ -63,6 +63,8 @@ def _load():
         lib.oracle_enhance.restype = None
         lib.oracle_alpha_layer.argtypes = [D, D, I, I]
         lib.oracle_alpha_layer.restype = D
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = I
         _lib = lib
     return _lib
 
@@ -80,6 +82,11 @@ def _np(x, dtype):
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def alpha_layer(alpha_base: float, cross_decay: float, layer: int, n_layers: int) -> float:

@@ -31,10 +31,14 @@
  * hand-computed fixtures); none is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* threads the OpenMP loops below use (reported with CPU timings) */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 #define IDX4(a, b, c, e, B_, C_, E_) ((((size_t)(a) * (B_) + (b)) * (C_) + (c)) * (E_) + (e))
 

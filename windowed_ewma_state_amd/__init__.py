@@ -1,0 +1,14 @@
+"""Signal Field Attention (SFA) for AMD Instinct MI355X (gfx950).
+
+Hand-written HIP kernels behind a C ABI (include/sfa.h, libsfa.so):
+  prefill      windowed softmax attention (last W <= 16 tokens) + far-field EWMA
+  decode_step  one token for all layers with the W-slot ring cache
+  enhance      optional triple-channel enhancement of an attention output
+PyTorch supplies device memory and streams only.
+"""
+from .sfa import (decode_step, enhance, enhance_workspace_size, prefill,  # noqa: F401
+                  prefill_workspace_size)
+from ._lib import SFAError  # noqa: F401
+
+__all__ = ["prefill", "decode_step", "enhance", "prefill_workspace_size",
+           "enhance_workspace_size", "SFAError"]

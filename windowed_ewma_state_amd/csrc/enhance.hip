@@ -1,0 +1,499 @@
+// enhance.hip -- optional triple-channel SFA enhancement for gfx950.
+//
+// Page "Dalin Soma SFA基于信号场注意力机制的神经网络推理加速框架":
+//   section 2.1 -- channel 1, ring buffer of the last 16 attention outputs
+//   (mean); channel 2, EMA field f = γ f + (1-γ) a with γ = 0.98; channel 3,
+//   64-slot semantic pool aggregated by attention at temperature 0.07;
+//   section 2.2 -- enhancement = ring_mean + 0.5·field + 0.5·semantic, clipped
+//   to ±ε, scaled by α_layer = α_base·(0.3 + 0.7·layer_ratio)·decay^layer and
+//   added to the attention output;
+//   section 2.4 -- the ring mean divides by the ring size.
+// Defaults (α_base 0.1, cross_decay 0.8, γ 0.98, 16 ring slots, 64 semantic
+// slots, clip 0.5) are the SFA_Config of page "Signal Field Attention (SFA)".
+//
+// Launches:
+//   k_pool_prep    pool -> bf16 hi/lo in the two MFMA operand orders, slot norms.
+//   k_field_agg    EMA of each 64-token tile from zero (a thread per 16-byte column chunk).
+//   k_field_carry  field before each tile (exclusive scan), final field.
+//   k_enhance      one wave per (layer, 64-token tile), four tiles per
+//                  workgroup, XCD-aware order:
+//                    cosine scores  C^T = pool · a^T   (MFMA, pool operand
+//                                   reused by the 4 token groups of 16),
+//                    softmax over the 64 slots in registers,
+//                    per 64-column chunk: ring-mean + field scan into LDS,
+//                    semantic sum   sem^T = pool^T · w^T (MFMA), clip, scale,
+//                                   add, store.
+//   k_ring_out     last min(R, T) attention rows -> ring (after all reads).
+// Precision: the fp32 pool and the softmax weights enter the MFMAs as bf16
+// hi + lo pairs (x = hi + lo to ~2^-17 relative); bf16 attention values are
+// exact, fp32 attention values are split the same way.
+#include <type_traits>
+
+#include "sfa_common.h"
+#include "sfa_internal.h"
+
+namespace sfa {
+
+namespace {
+
+constexpr int kSlots = 64;
+constexpr int kCols = 64;          // columns per epilogue chunk (one per lane)
+constexpr int kTilesPerBlock = 4;  // waves (64-token tiles) per workgroup
+constexpr int kOpElems = 64 * 8;   // one MFMA operand (64 lanes x 8 bf16)
+
+__device__ __forceinline__ float alpha_layer(float base, float decay, int layer, int n_layers) {
+    const float ratio = n_layers > 1 ? (float)layer / (float)(n_layers - 1) : 0.f;
+    return base * (0.3f + 0.7f * ratio) * powf(decay, (float)layer);
+}
+
+__device__ __forceinline__ void split8(const float *v, uint16_t *hi, uint16_t *lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)v[e];
+        const __bf16 l = (__bf16)(v[e] - (float)h);
+        hi[e] = __builtin_bit_cast(uint16_t, h);
+        lo[e] = __builtin_bit_cast(uint16_t, l);
+    }
+}
+__device__ __forceinline__ void put8(uint16_t *dst, const uint16_t *v) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)v[2 * i] | ((uint32_t)v[2 * i + 1] << 16);
+    *reinterpret_cast<u32x4 *>(dst) = w;
+}
+__device__ __forceinline__ bf16x8 get8(const uint16_t *src) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src));
+}
+
+// ---------------------------------------------------------------------------
+// k_pool_prep.  Per pool layer pl:
+//   poolA[pl][ks][j][hl][lane][8]: slot 16j + lane%16, x = 32ks + 8(lane/16) + e
+//       (A operand of the cosine scores, k = hidden dim)
+//   poolT[pl][xg][ks][hl][lane][8]: x = 16xg + lane%16,
+//       slot = 32ks + (e<4 ? 4(lane/16)+e : 16+4(lane/16)+e-4)
+//       (A operand of the semantic sum, k = slot)
+//   slot_norm[pl][slot] = max(|s|, 1e-12)
+// One workgroup per (pool layer, 32-column step); 256 threads = 4 j x 64 lanes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pool_prep(EnhanceArgs a) {
+    const int ksteps = a.H / 32;
+    const int pl = blockIdx.x / ksteps, ks = blockIdx.x % ksteps;
+    const float *P = a.pool + (long)pl * a.pool_stride;
+    const int j = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int q4 = lane / 16, c16 = lane % 16;
+    uint16_t *poolA = a.poolA + (long)pl * ksteps * 4 * 2 * kOpElems;
+    uint16_t *poolT = a.poolT + (long)pl * (a.H / 16) * 2 * 2 * kOpElems;
+    uint16_t hi[8], lo[8];
+    {   // cosine operand
+        const int slot = 16 * j + c16;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = slot < a.n_slots ? P[(long)slot * a.H + 32 * ks + 8 * q4 + e] : 0.f;
+        split8(v, hi, lo);
+        uint16_t *dst = poolA + (((long)ks * 4 + j) * 2) * kOpElems + lane * 8;
+        put8(dst, hi);
+        put8(dst + kOpElems, lo);
+    }
+    if (j < 2) {  // semantic operand for the two 16-column tiles of this step
+        const int xg = 2 * ks + j;
+        const int x = 16 * xg + c16;
+#pragma unroll
+        for (int sk = 0; sk < 2; ++sk) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int slot = 32 * sk + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + e - 4);
+                v[e] = slot < a.n_slots ? P[(long)slot * a.H + x] : 0.f;
+            }
+            split8(v, hi, lo);
+            uint16_t *dst = poolT + (((long)xg * 2 + sk) * 2) * kOpElems + lane * 8;
+            put8(dst, hi);
+            put8(dst + kOpElems, lo);
+        }
+    }
+    if (ks == 0) {  // slot norms: 4 threads per slot
+        const int slot = threadIdx.x / 4, part = threadIdx.x % 4;
+        float ss = 0.f;
+        if (slot < a.n_slots)
+            for (int x = part; x < a.H; x += 4) {
+                const float v = P[(long)slot * a.H + x];
+                ss = fmaf(v, v, ss);
+            }
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        if (part == 0) a.slot_norm[pl * kSlots + slot] = fmaxf(sqrtf(ss), 1e-12f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_field_agg: EMA of each 64-token tile from zero.  A thread owns one 16-byte
+// column chunk and scans the tile's tokens in batches of 16 loads in flight.
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__global__ __launch_bounds__(256) void k_field_agg(EnhanceArgs a) {
+    constexpr int EPC = 16 / sizeof(TIn);
+    const int H = a.H, T = a.T;
+    const int chunks = H / EPC;
+    const int cpb = (chunks + 255) / 256;  // workgroups per (layer, tile)
+    const int tl = blockIdx.x / cpb;
+    const int ch = (blockIdx.x % cpb) * 256 + threadIdx.x;
+    if (ch >= chunks) return;
+    const int tile = tl % a.ntiles, l = tl / a.ntiles;
+    const float g = a.ema_gamma;
+    const int t0 = tile * kTile, len = min(kTile, T - t0);
+    const TIn *A = reinterpret_cast<const TIn *>(a.attn) + ((long)l * T + t0) * H + ch * EPC;
+    float f[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) f[e] = 0.f;
+    for (int j0 = 0; j0 < len; j0 += kBlk) {
+        u32x4 raw[kBlk];
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            raw[j] = u32x4{0u, 0u, 0u, 0u};
+            if (j0 + j < len) raw[j] = *reinterpret_cast<const u32x4 *>(A + (long)(j0 + j) * H);
+        }
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            const float keep = (j0 + j < len) ? 1.f : 0.f;  // past the end: f unchanged
+            float v[EPC];
+            if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = bf16_lo(raw[j][i]);
+                    v[2 * i + 1] = bf16_hi(raw[j][i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(raw[j][i]);
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                const float nf = g * f[e] + (1.f - g) * v[e];
+                f[e] = keep != 0.f ? nf : f[e];
+            }
+        }
+    }
+    float *dst = a.agg64 + ((long)l * a.ntiles + tile) * H + ch * EPC;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) dst[e] = f[e];
+}
+
+// ---------------------------------------------------------------------------
+// k_field_carry: field before each tile and the final field (thread per column)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_field_carry(EnhanceArgs a) {
+    const int cpb = (a.H + 255) / 256;
+    const int l = blockIdx.x / cpb;
+    const int x = (blockIdx.x % cpb) * 256 + threadIdx.x;
+    if (x >= a.H) return;
+    const float g = a.ema_gamma;
+    const float gfull = powi(g, kTile);
+    float F = a.field[(long)l * a.H + x];
+    const float *A = a.agg64 + (long)l * a.ntiles * a.H + x;
+    float *C = a.carry + (long)l * a.ntiles * a.H + x;
+    for (int i0 = 0; i0 < a.ntiles; i0 += kBlk) {
+        float ag[kBlk];
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) ag[j] = (i0 + j < a.ntiles) ? A[(long)(i0 + j) * a.H] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            const int i = i0 + j;
+            if (i < a.ntiles) {
+                C[(long)i * a.H] = F;
+                const int len = min(kTile, a.T - i * kTile);
+                const float gl = len == kTile ? gfull : powi(g, len);
+                F = gl * F + ag[j];
+            }
+        }
+    }
+    a.field[(long)l * a.H + x] = F;
+}
+
+// ---------------------------------------------------------------------------
+// k_enhance
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__device__ __forceinline__ void load_a8(const TIn *p, bf16x8 &hi, bf16x8 &lo, float &sq);
+template <>
+__device__ __forceinline__ void load_a8<__bf16>(const __bf16 *p, bf16x8 &hi, bf16x8 &lo, float &sq) {
+    hi = *reinterpret_cast<const bf16x8 *>(p);
+    lo = bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float v = (float)hi[e];
+        sq = fmaf(v, v, sq);
+    }
+}
+template <>
+__device__ __forceinline__ void load_a8<float>(const float *p, bf16x8 &hi, bf16x8 &lo, float &sq) {
+    const float4 v0 = *reinterpret_cast<const float4 *>(p);
+    const float4 v1 = *reinterpret_cast<const float4 *>(p + 4);
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        __bf16 h, l;
+        split_bf16(v[e], h, l);
+        hi[e] = h;
+        lo[e] = l;
+        sq = fmaf(v[e], v[e], sq);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 load4f(const T *p);
+template <>
+__device__ __forceinline__ f32x4 load4f<float>(const float *p) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    return f32x4{v.x, v.y, v.z, v.w};
+}
+template <>
+__device__ __forceinline__ f32x4 load4f<__bf16>(const __bf16 *p) {
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+    return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+}
+
+template <typename TOut>
+__device__ __forceinline__ void store4o(TOut *p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4o<float>(float *p, f32x4 v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ void store4o<__bf16>(__bf16 *p, f32x4 v) {
+    u32x2 w;
+    w[0] = pack_bf16x2(v[0], v[1]);
+    w[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2 *>(p) = w;
+}
+
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void k_enhance(EnhanceArgs a) {
+    constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split everything
+    constexpr int XS = kCols + 4;                                // LDS row stride (floats)
+    __shared__ __attribute__((aligned(16))) float Xl[kTilesPerBlock][kTile * XS];  // rm/R + 0.5·field
+
+    const int groups = (a.ntiles + kTilesPerBlock - 1) / kTilesPerBlock;
+    const int lid = xcd_remap(blockIdx.x, a.L * groups);
+    const int l = lid / groups;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tile = (lid % groups) * kTilesPerBlock + wave;
+    if (tile >= a.ntiles) return;  // wave-uniform; the kernel has no workgroup barrier
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const int H = a.H, T = a.T, R = a.R;
+    const int tb = tile * kTile;
+    const int pl = a.pool_stride == 0 ? 0 : l;
+    const int ksteps = H / 32;
+    const uint16_t *poolA = a.poolA + (long)pl * ksteps * 4 * 2 * kOpElems + lane * 8;
+    const uint16_t *poolT = a.poolT + (long)pl * (H / 16) * 2 * 2 * kOpElems + lane * 8;
+    const float *snorm = a.slot_norm + pl * kSlots;
+    const TIn *Ag = reinterpret_cast<const TIn *>(a.attn) + (long)l * T * H;
+    const float al = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
+    const int nj = (a.n_slots + 15) / 16;
+
+    // ---- (1) cosine scores: lane holds C^T[slot 16j+4q4+i][token tb+16tg+c16] ----
+    f32x4 C[4][4];
+    float sq[4];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+        sq[tg] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) C[j][tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const TIn *arow[4];
+    bool tok_ok[4];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+        const int t = tb + 16 * tg + c16;
+        tok_ok[tg] = t < T;
+        arow[tg] = Ag + (long)(tok_ok[tg] ? t : tb) * H + 8 * q4;
+    }
+    for (int ks = 0; ks < ksteps; ++ks) {
+        bf16x8 bh[4], bl[4];
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) load_a8<TIn>(arow[tg] + 32 * ks, bh[tg], bl[tg], sq[tg]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < nj) {
+                const uint16_t *op = poolA + (((long)ks * 4 + j) * 2) * kOpElems;
+                const bf16x8 ph = get8(op);
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) C[j][tg] = mfma_bf16_16x16x32(ph, bh[tg], C[j][tg]);
+                const bf16x8 plo = get8(op + kOpElems);
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) C[j][tg] = mfma_bf16_16x16x32(plo, bh[tg], C[j][tg]);
+                if constexpr (kPrecise) {
+#pragma unroll
+                    for (int tg = 0; tg < 4; ++tg) C[j][tg] = mfma_bf16_16x16x32(ph, bl[tg], C[j][tg]);
+                }
+            }
+        }
+    }
+
+    // ---- (2) softmax over slots; w as the B operand of the semantic sum -----------
+    // k-step ks of the semantic sum holds slot tiles 2ks (e<4) and 2ks+1 (e>=4)
+    bf16x8 Wh[4][2], Wl[4][2];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+        const float inv_na = 1.f / fmaxf(sqrtf(sum_over_groups(sq[tg])), 1e-12f);
+        float w[16], m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int slot = 16 * j + 4 * q4 + i;
+                w[4 * j + i] = slot < a.n_slots ? C[j][tg][i] * inv_na / snorm[slot] * a.inv_temp_log2e
+                                                : -INFINITY;
+                m = fmaxf(m, w[4 * j + i]);
+            }
+        m = max_over_groups(m);
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            w[k] = (16 * (k >> 2) + 4 * q4 + (k & 3) < a.n_slots) ? exp2f(w[k] - m) : 0.f;
+            sum += w[k];
+        }
+        const float inv = 1.f / sum_over_groups(sum);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 h, lo_;
+                split_bf16(w[4 * (2 * ks + (e >> 2)) + (e & 3)] * inv, h, lo_);
+                Wh[tg][ks][e] = h;
+                Wl[tg][ks][e] = lo_;
+            }
+    }
+
+    // ---- (3) per 64-column chunk: ring mean + field scan, semantic sum, epilogue ---
+    const float g = a.ema_gamma;
+    const float invR = 1.f / (float)R;
+    const int len = min(kTile, T - tb);
+    const float *ringl = a.ring + (long)l * R * H;
+    const float *carry = a.carry + ((long)l * a.ntiles + tile) * H;
+    float *Xw = Xl[wave];
+    TOut *Og = reinterpret_cast<TOut *>(a.out) + (long)l * T * H;
+    float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
+
+    for (int xc = 0; xc < H; xc += kCols) {
+        const int x = xc + lane;
+        // value of relative token t at column x (t >= -R: the carried ring)
+        auto val = [&](int t) -> float {
+            if (t >= 0) return t < T ? Elem<TIn>::load(Ag + (long)t * H + x) : 0.f;
+            const int slot = (int)((((long)a.t0 + t) % R + R) % R);
+            return ringl[(long)slot * H + x];
+        };
+        // ring sum of tokens tb-R .. tb-1, then slide: + token j, - token j-R
+        float rs = 0.f;
+        {
+            float pre[kBlk];
+#pragma unroll
+            for (int k = 0; k < kBlk; ++k) pre[k] = (k < R) ? val(tb - 1 - k) : 0.f;
+#pragma unroll
+            for (int k = 0; k < kBlk; ++k) rs += pre[k];
+        }
+        float F = carry[x];
+        for (int j0 = 0; j0 < len; j0 += kBlk) {
+            float cur[kBlk], old[kBlk];
+#pragma unroll
+            for (int j = 0; j < kBlk; ++j) {  // the batch's loads are all in flight together
+                const bool ok = j0 + j < len;
+                cur[j] = ok ? val(tb + j0 + j) : 0.f;
+                old[j] = ok ? val(tb + j0 + j - R) : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kBlk; ++j) {
+                if (j0 + j < len) {
+                    rs += cur[j] - old[j];
+                    F = g * F + (1.f - g) * cur[j];
+                    Xw[(j0 + j) * XS + lane] = rs * invR + 0.5f * F;
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+        for (int xt = 0; xt < kCols / 16; ++xt) {
+            const int xg = xc / 16 + xt;
+            const uint16_t *op = poolT + ((long)xg * 2 * 2) * kOpElems;
+            const bf16x8 th0 = get8(op), th1 = get8(op + 2 * kOpElems);
+            const bf16x8 tl0 = get8(op + kOpElems), tl1 = get8(op + 3 * kOpElems);
+            const int xl = 16 * xt + 4 * q4;
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) {
+                f32x4 s = {0.f, 0.f, 0.f, 0.f};
+                s = mfma_bf16_16x16x32(th0, Wh[tg][0], s);
+                s = mfma_bf16_16x16x32(th0, Wl[tg][0], s);
+                s = mfma_bf16_16x16x32(th1, Wh[tg][1], s);
+                s = mfma_bf16_16x16x32(th1, Wl[tg][1], s);
+                s = mfma_bf16_16x16x32(tl0, Wh[tg][0], s);
+                s = mfma_bf16_16x16x32(tl1, Wh[tg][1], s);
+                // lane: sem[x = xc + xl + i][token tb + 16tg + c16]
+                const int jt = 16 * tg + c16;
+                if (tok_ok[tg]) {
+                    const f32x4 X4 = *reinterpret_cast<const f32x4 *>(&Xw[jt * XS + xl]);
+                    const long off = (long)(tb + jt) * H + xc + xl;
+                    const f32x4 A4 = load4f<TIn>(Ag + off);
+                    f32x4 o, en;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = fminf(fmaxf(X4[i] + 0.5f * s[i], -a.clip), a.clip);
+                        en[i] = al * e;
+                        o[i] = A4[i] + en[i];
+                    }
+                    store4o<TOut>(Og + off, o);
+                    if (Eg) store4o<float>(Eg + off, en);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// last min(R, T) attention rows -> ring slots (t0 + t) mod R
+template <typename TIn>
+__global__ __launch_bounds__(256) void k_ring_out(EnhanceArgs a) {
+    const int l = blockIdx.x;
+    const int first = max(0, a.T - a.R);
+    const long cnt = (long)(a.T - first) * a.H;
+    const TIn *A = reinterpret_cast<const TIn *>(a.attn) + (long)l * a.T * a.H;
+    float *ring = a.ring + (long)l * a.R * a.H;
+    for (long idx = threadIdx.x; idx < cnt; idx += 256) {
+        const int t = first + (int)(idx / a.H);
+        const int x = (int)(idx % a.H);
+        ring[(long)(((long)a.t0 + t) % a.R) * a.H + x] = Elem<TIn>::load(A + (long)t * a.H + x);
+    }
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
+    const int groups = (a.ntiles + kTilesPerBlock - 1) / kTilesPerBlock;
+    hipLaunchKernelGGL(k_pool_prep, dim3(a.n_pool_layers * (a.H / 32)), dim3(256), 0, stream, a);
+    const int fchunks = a.H / (16 / (int)sizeof(TIn));
+    hipLaunchKernelGGL((k_field_agg<TIn>), dim3(a.L * a.ntiles * ((fchunks + 255) / 256)), dim3(256), 0,
+                       stream, a);
+    hipLaunchKernelGGL(k_field_carry, dim3(a.L * ((a.H + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_enhance<TIn, TOut>), dim3(a.L * groups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_ring_out<TIn>), dim3(a.L), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers) {
+    const size_t nt = (size_t)((T + kTile - 1) / kTile);
+    const size_t floats = 2 * (size_t)L * nt * H + (size_t)n_pool_layers * kSlots;
+    // poolA and poolT: H/32 steps x 4 tiles (resp. H/16 x 2 steps) x hi/lo x 512 bf16
+    const size_t ops = (size_t)n_pool_layers * (size_t)H * 64 * 2 * 2;
+    return floats * sizeof(float) + ops * sizeof(uint16_t);
+}
+
+hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream) {
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_t<__bf16, __bf16>(a, stream) : launch_t<__bf16, float>(a, stream);
+    return a.out_bf16 ? launch_t<float, __bf16>(a, stream) : launch_t<float, float>(a, stream);
+}
+
+}  // namespace sfa

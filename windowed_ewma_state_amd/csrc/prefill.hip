@@ -1,0 +1,586 @@
+// prefill.hip -- SFA prefill for gfx950: causal sliding-window attention over
+// the last W <= 16 tokens plus the far-field EWMA of the keys that leave the
+// window, fused as O = O_near + α·S_t.
+//
+// Page "Signal Field Attention (SFA)：8KB代码实现4.16倍推理加速与248倍内存压缩",
+// section 2.1: near-field equation (softmax(q·K_near^T/sqrt(d))·V_near over
+// the most recent k tokens), far-field equation (S_t = γ S_{t-1} + (1-γ)·key
+// leaving the window) and the fusion equation; section 2.2 (O(k·n·d) time).
+//
+// Three launches per call:
+//   k_ewma_agg    one workgroup per (b, KV head, 64-token tile): local EWMA
+//                 aggregate of each 16-token block and of the tile (scan from 0).
+//   k_ewma_carry  one workgroup per (b, KV head): exclusive scan of the tile
+//                 aggregates -> S just before every tile; writes the final S.
+//   k_window_attn one workgroup per (b, KV head, tile), XCD-aware order:
+//                 stages K rows [t0-16, t0+64) row-major and V transposed in
+//                 LDS, shared by all query heads of the GQA group; each wave
+//                 owns 16 tokens: EWMA scan from its carry, then per head
+//                 8 score MFMAs (two 16-key tiles) + 16 PV MFMAs (P split into
+//                 bf16 hi + lo) and the α·S epilogue.
+// A fourth, tiny launch copies the last W keys/values into the ring when the
+// call continues an existing cache (the first tile reads the old ring).
+#include <type_traits>
+
+#include "sfa_common.h"
+#include "sfa_internal.h"
+
+namespace sfa {
+
+namespace {
+
+constexpr int kRows = kTile + kMaxWindow;  // staged rows: tokens t0-16 .. t0+63
+
+// pointer to the key/value row of relative token index t (t < 0 reads the ring
+// of a continued sequence; returns nullptr when the position does not exist)
+template <typename T>
+__device__ __forceinline__ const T *kv_row(const T *x_bg, long row_stride, const T *ring_bg, int t,
+                                           int n, int p0, int W, int D) {
+    if (t >= 0) return t < n ? x_bg + (long)t * row_stride : nullptr;
+    const int pos = p0 + t;
+    if (pos < 0 || ring_bg == nullptr) return nullptr;
+    return ring_bg + (long)(pos % W) * D;
+}
+
+template <typename T, int EPL>
+__device__ __forceinline__ void load_epl(const T *p, float *x) {
+    if constexpr (EPL == 2) {
+        load2(p, x[0], x[1]);
+    } else {
+        x[0] = Elem<T>::load(p);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_ewma_agg: local aggregates A (EWMA from zero) of 16-token blocks and tiles.
+// One wave per 64-token tile (four tiles per workgroup).  Lane (w, c) owns the
+// 16-byte chunk c of the head dimension for block w of the tile, so every load
+// is a 16-byte vector and a block's 16 rows are in flight together.
+// ---------------------------------------------------------------------------
+template <typename TIn, int D>
+__global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
+    constexpr int EPC = 16 / sizeof(TIn);  // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;           // chunks per row (8 or 16 for bf16, 16 or 32 for fp32)
+    constexpr int LPB = 64 / 4;            // lanes per block: 16
+    constexpr int CPL = CPR / LPB > 0 ? CPR / LPB : 1;  // chunks per lane
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tiles_per_bg = a.ntiles;
+    const int gt = blockIdx.x * 4 + wave;  // global tile index over (bg, tile)
+    if (gt >= a.B * a.Hkv * tiles_per_bg) return;
+    const int tile = gt % tiles_per_bg, bg = gt / tiles_per_bg;
+    const int b = bg / a.Hkv, G = bg % a.Hkv;
+    const int n = a.n, W = a.W;
+    const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
+    const float gm = a.gamma[G];
+    const long row_stride = (long)a.Hkv * D;
+    const TIn *Kbg = reinterpret_cast<const TIn *>(a.k) + ((long)b * n * a.Hkv + G) * D;
+    const TIn *ringK = a.pos0 ? reinterpret_cast<const TIn *>(a.ring_k) + (long)bg * W * D : nullptr;
+    const int blk = lane / LPB, c0 = lane % LPB;
+    const int tb = tile * kTile + kBlk * blk;
+    const bool lane_ok = c0 < CPR;  // d = 64 bf16 has 8 chunks per row: half the lanes idle
+
+    float A[CPL][EPC];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) A[cc][e] = 0.f;
+    if (lane_ok) {
+        u32x4 raw[kBlk][CPL];
+        bool use[kBlk];
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            const int t = tb + j;
+            use[j] = (t < n) && (p0 + t >= W);
+            const TIn *row = use[j] ? kv_row(Kbg, row_stride, ringK, t - W, n, p0, W, D) : nullptr;
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                raw[j][cc] = u32x4{0u, 0u, 0u, 0u};
+                if (row) raw[j][cc] = *reinterpret_cast<const u32x4 *>(row + (c0 + LPB * cc) * EPC);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            if (!use[j]) continue;
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                float v[EPC];
+                if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] = bf16_lo(raw[j][cc][i]);
+                        v[2 * i + 1] = bf16_hi(raw[j][cc][i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(raw[j][cc][i]);
+                }
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) A[cc][e] = gm * A[cc][e] + (1.f - gm) * v[e];
+            }
+        }
+    }
+    // 16-token block aggregates, then the tile aggregate: blocks combined in
+    // order through LDS, T = ((A0·g1 + A1)·g2 + A2)·g3 + A3 with g_w the decay
+    // over block w's evicting steps
+    float *a16 = a.agg16 + (((long)bg * a.ntiles + tile) * 4 + blk) * D;
+    const int blen = max(0, min(kBlk, n - tb));
+    const int steps = max(0, blen - max(0, W - p0 - tb));
+    const float gl = powi(gm, steps);
+    if (lane_ok) {
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) a16[(c0 + LPB * cc) * EPC + e] = A[cc][e];
+    }
+    __shared__ float blkv[4][4][D];  // [wave][block][d]
+    if (lane_ok) {
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) blkv[wave][blk][(c0 + LPB * cc) * EPC + e] = A[cc][e];
+    }
+    __shared__ float decay[4][4];
+    if (c0 == 0) decay[wave][blk] = gl;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float *a64 = a.agg64 + ((long)bg * a.ntiles + tile) * D;
+    for (int e = lane; e < D; e += 64) {
+        float T = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) T = decay[wave][w] * T + blkv[wave][w][e];
+        a64[e] = T;
+    }
+}
+
+// number of evicting steps (positions >= W) among tokens [s0, s0+len)
+__device__ __forceinline__ int evict_steps(int p0, int s0, int len, int W) {
+    const int first = max(s0, W - p0);  // first relative token with p0 + t >= W
+    return max(0, s0 + len - max(first, s0));
+}
+
+// ---------------------------------------------------------------------------
+// k_ewma_carry: S before each tile (exclusive scan over tiles) and final S.
+// One workgroup per (b, KV head, 16 head-dim elements); 64 parts of the tile
+// range are scanned in parallel (all loads of a part issued together), the
+// part aggregates are combined through LDS, and each part is rescanned from
+// its carry-in.
+// ---------------------------------------------------------------------------
+constexpr int kCarryParts = 64, kCarryCols = 16;
+
+__global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
+    __shared__ float partX[kCarryParts][kCarryCols];
+    __shared__ float partG[kCarryParts];
+    const int D = a.d;
+    const int cblocks = D / kCarryCols;
+    const int bg = blockIdx.x / cblocks;
+    const int e = (blockIdx.x % cblocks) * kCarryCols + threadIdx.x % kCarryCols;
+    const int part = threadIdx.x / kCarryCols;
+    const int b = bg / a.Hkv, G = bg % a.Hkv;
+    const int n = a.n, W = a.W, nt = a.ntiles;
+    const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
+    const float gm = a.gamma[G];
+    const float S_init = (a.pos0 && p0 > 0) ? a.state[(long)bg * D + e] : 0.f;
+    const float g64 = powi(gm, kTile);
+
+    const int per = (nt + kCarryParts - 1) / kCarryParts;
+    const int i0 = min(part * per, nt), i1 = min(i0 + per, nt);
+    const float *A = a.agg64 + (long)bg * nt * D + e;
+    auto decay_of = [&](int i) {
+        const int len = min(kTile, n - i * kTile);
+        const int st = evict_steps(p0, i * kTile, len, W);
+        return st == kTile ? g64 : powi(gm, st);
+    };
+    float X = 0.f, Gam = 1.f;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+        const float gl = decay_of(i);
+        X = gl * X + A[(long)i * D];
+        Gam *= gl;
+    }
+    partX[part][threadIdx.x % kCarryCols] = X;
+    if (threadIdx.x % kCarryCols == 0) partG[part] = Gam;
+    __syncthreads();
+    float C = S_init;
+    for (int q = 0; q < part; ++q) C = partG[q] * C + partX[q][threadIdx.x % kCarryCols];
+    float *Cout = a.carry + (long)bg * nt * D + e;
+    X = C;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+        Cout[(long)i * D] = X;
+        X = decay_of(i) * X + A[(long)i * D];
+    }
+    if (part == kCarryParts - 1 && a.state) a.state[(long)bg * D + e] = X;
+}
+
+// ---------------------------------------------------------------------------
+// k_window_attn: windowed softmax attention + α·S epilogue
+// ---------------------------------------------------------------------------
+template <typename TIn> struct Lds;
+template <> struct Lds<__bf16> { static constexpr int kpad = 8, vpad = 8; };
+template <> struct Lds<float> { static constexpr int kpad = 4, vpad = 4; };
+
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut *p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float *p, f32x4 v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16 *p, f32x4 v) {
+    u32x2 w;
+    w[0] = pack_bf16x2(v[0], v[1]);
+    w[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2 *>(p) = w;
+}
+
+template <typename TIn, typename TOut, int D>
+__global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
+    constexpr bool kBf16 = std::is_same<TIn, __bf16>::value;
+    constexpr int EPL = D / kWave;
+    constexpr int KS = D + Lds<TIn>::kpad;      // Klds row stride (elements)
+    constexpr int VS = kRows + Lds<TIn>::vpad;  // Vt row stride (elements)
+    constexpr int SS = D + 4;                   // Sb row stride (floats)
+    constexpr int EPC = 16 / sizeof(TIn);       // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;                // chunks per row
+
+    __shared__ __attribute__((aligned(16))) TIn Klds[kRows * KS];
+    __shared__ __attribute__((aligned(16))) TIn Vt[D * VS];
+    __shared__ __attribute__((aligned(16))) float Sb[4][kBlk * SS];
+
+    const int nblk = a.B * a.Hkv * a.ntiles;
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int tile = lid % a.ntiles;
+    const int bg = lid / a.ntiles;
+    const int b = bg / a.Hkv, G = bg % a.Hkv;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const int n = a.n, W = a.W, group = a.group;
+    const int t0 = tile * kTile;
+    const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
+    const float gm = a.gamma[G];
+
+    const long row_stride = (long)a.Hkv * D;
+    const TIn *Kbg = reinterpret_cast<const TIn *>(a.k) + ((long)b * n * a.Hkv + G) * D;
+    const TIn *Vbg = reinterpret_cast<const TIn *>(a.v) + ((long)b * n * a.Hkv + G) * D;
+    const bool cont = a.pos0 != nullptr;
+    const TIn *ringKr = cont ? reinterpret_cast<const TIn *>(a.ring_k) + (long)bg * a.W * D : nullptr;
+    const TIn *ringVr = cont ? reinterpret_cast<const TIn *>(a.ring_v) + (long)bg * a.W * D : nullptr;
+    // a fresh prompt hands its last W keys/values to the ring here
+    const bool write_ring = !cont && a.ring_k != nullptr;
+    TIn *ringKw = write_ring ? reinterpret_cast<TIn *>(a.ring_k) + (long)bg * a.W * D : nullptr;
+    TIn *ringVw = write_ring ? reinterpret_cast<TIn *>(a.ring_v) + (long)bg * a.W * D : nullptr;
+
+    // ---- (1) stage K rows (row-major) and V (transposed) ---------------------
+    for (int idx = tid; idx < kRows * CPR; idx += 256) {
+        const int r = idx / CPR, c = idx % CPR;
+        const int t = t0 - kMaxWindow + r;
+        const TIn *src = kv_row(Kbg, row_stride, ringKr, t, n, p0, W, D);
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (src) val = *reinterpret_cast<const u32x4 *>(src + c * EPC);
+        *reinterpret_cast<u32x4 *>(&Klds[r * KS + c * EPC]) = val;
+        if (write_ring && t >= t0 && t < n && t >= n - W)
+            *reinterpret_cast<u32x4 *>(ringKw + (long)(t % W) * D + c * EPC) = val;
+    }
+    if constexpr (kBf16) {
+        // two keys per thread so each LDS write is one aligned dword
+        for (int idx = tid; idx < (kRows / 2) * CPR; idx += 256) {
+            const int m = idx / CPR, c = idx % CPR;
+            const int ta = t0 - kMaxWindow + 2 * m;
+            const TIn *sa = kv_row(Vbg, row_stride, ringVr, ta, n, p0, W, D);
+            const TIn *sb = kv_row(Vbg, row_stride, ringVr, ta + 1, n, p0, W, D);
+            u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+            if (sa) va = *reinterpret_cast<const u32x4 *>(sa + c * EPC);
+            if (sb) vb = *reinterpret_cast<const u32x4 *>(sb + c * EPC);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
+                const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
+                *reinterpret_cast<uint32_t *>(&Vt[(c * EPC + 2 * i) * VS + 2 * m]) = lo;
+                *reinterpret_cast<uint32_t *>(&Vt[(c * EPC + 2 * i + 1) * VS + 2 * m]) = hi;
+            }
+            if (write_ring) {
+                if (ta >= t0 && ta < n && ta >= n - W)
+                    *reinterpret_cast<u32x4 *>(ringVw + (long)(ta % W) * D + c * EPC) = va;
+                if (ta + 1 >= t0 && ta + 1 < n && ta + 1 >= n - W)
+                    *reinterpret_cast<u32x4 *>(ringVw + (long)((ta + 1) % W) * D + c * EPC) = vb;
+            }
+        }
+    } else {
+        for (int idx = tid; idx < kRows * CPR; idx += 256) {
+            const int r = idx / CPR, c = idx % CPR;
+            const int t = t0 - kMaxWindow + r;
+            const TIn *src = kv_row(Vbg, row_stride, ringVr, t, n, p0, W, D);
+            float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (src) val = *reinterpret_cast<const float4 *>(src + c * EPC);
+            Vt[(c * EPC + 0) * VS + r] = val.x;
+            Vt[(c * EPC + 1) * VS + r] = val.y;
+            Vt[(c * EPC + 2) * VS + r] = val.z;
+            Vt[(c * EPC + 3) * VS + r] = val.w;
+            if (write_ring && t >= t0 && t < n && t >= n - W)
+                *reinterpret_cast<float4 *>(ringVw + (long)(t % W) * D + c * EPC) = val;
+        }
+    }
+
+    // ---- (2) S just before this wave's 16-token block -----------------------
+    const int e0 = lane * EPL;
+    float S[EPL];
+    {
+        const long tbase = (long)bg * a.ntiles + tile;
+        const float *C = a.carry + tbase * D + e0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) S[e] = C[e];
+        for (int w = 0; w < wave; ++w) {
+            const int s0 = t0 + kBlk * w;
+            const float gl = powi(gm, evict_steps(p0, s0, min(kBlk, n - s0), W));
+            const float *A = a.agg16 + (tbase * 4 + w) * D + e0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) S[e] = gl * S[e] + A[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- (3) EWMA through the block: S_t after token t's own eviction ---------
+    const int tb = t0 + kBlk * wave;
+    float *Sw = Sb[wave];
+#pragma unroll
+    for (int j = 0; j < kBlk; ++j) {
+        const int t = tb + j;
+        if (t < n && p0 + t >= W) {
+            // token t - W sits in staged row (t - W) - (t0 - 16)
+            const TIn *kr = &Klds[(kBlk * wave + j + kMaxWindow - W) * KS + e0];
+            float kv[EPL];
+            load_epl<TIn, EPL>(kr, kv);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) Sw[j * SS + e0 + e] = S[e];
+    }
+    __syncthreads();
+
+    // ---- (4) per-wave operand caches, shared by every head of the group ------
+    // key tiles: T0 = staged rows 16*wave + [0,16), T1 = 16*wave + 16 + [0,16)
+    // (keys tb-16 .. tb+15); row c16 of each tile is this lane's A row.
+    f32x4 Sc[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        Sc[dt] = *reinterpret_cast<const f32x4 *>(&Sw[c16 * SS + 16 * dt + 4 * q4]);
+
+    // score-validity mask: element T*4+i is key (tb-16) + 16T + 4*q4 + i for token tb + c16
+    const int tok = tb + c16;
+    const bool tok_ok = tok < n;
+    unsigned mask = 0;
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kr = tb - kMaxWindow + 16 * T + 4 * q4 + i;
+            if (kr <= tok && kr > tok - W && p0 + kr >= 0) mask |= 1u << (4 * T + i);
+        }
+
+    const TIn *Qtok = reinterpret_cast<const TIn *>(a.q) + (((long)b * n + tok) * a.Hq + (long)G * group) * D;
+    TOut *Otok = reinterpret_cast<TOut *>(a.out) + (((long)b * n + tok) * a.Hq + (long)G * group) * D;
+    const float *alpha = a.alpha + (long)G * group;
+
+    if constexpr (kBf16) {
+        bf16x8 Kc[2][D / 32];
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int st = 0; st < D / 32; ++st)
+                Kc[T][st] = *reinterpret_cast<const bf16x8 *>(
+                    &Klds[(kBlk * wave + 16 * T + c16) * KS + 32 * st + 8 * q4]);
+        bf16x8 Vc[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const TIn *vr = &Vt[(16 * dt + c16) * VS + kBlk * wave + 4 * q4];
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
+            const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
+            u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+            Vc[dt] = __builtin_bit_cast(bf16x8, w);
+        }
+
+        bf16x8 Qn[D / 32];
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) {
+            Qn[st] = bf16x8{};
+            if (tok_ok) Qn[st] = *reinterpret_cast<const bf16x8 *>(Qtok + 32 * st + 8 * q4);
+        }
+        for (int hh = 0; hh < group; ++hh) {
+            bf16x8 Qc[D / 32];
+#pragma unroll
+            for (int st = 0; st < D / 32; ++st) Qc[st] = Qn[st];
+            if (hh + 1 < group) {  // prefetch the next head's queries
+#pragma unroll
+                for (int st = 0; st < D / 32; ++st)
+                    if (tok_ok) Qn[st] = *reinterpret_cast<const bf16x8 *>(Qtok + (long)(hh + 1) * D + 32 * st + 8 * q4);
+            }
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+            for (int st = 0; st < D / 32; ++st) {
+                s0 = mfma_bf16_16x16x32(Kc[0][st], Qc[st], s0);
+                s1 = mfma_bf16_16x16x32(Kc[1][st], Qc[st], s1);
+            }
+            float x[8], m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (mask >> i & 1) ? s0[i] * a.scale_log2e : -INFINITY;
+                x[4 + i] = (mask >> (4 + i) & 1) ? s1[i] * a.scale_log2e : -INFINITY;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, x[i]);
+            m = max_over_groups(m);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = (mask >> i & 1) ? exp2f(x[i] - m) : 0.f;
+                sum += x[i];
+            }
+            sum = sum_over_groups(sum);
+            const float inv = 1.f / sum;
+            bf16x8 Ph, Pl;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __bf16 h, l;
+                split_bf16(x[i] * inv, h, l);
+                Ph[i] = h;
+                Pl[i] = l;
+            }
+            const float al = alpha[hh];
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                o = mfma_bf16_16x16x32(Vc[dt], Ph, o);
+                o = mfma_bf16_16x16x32(Vc[dt], Pl, o);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = fmaf(al, Sc[dt][i], o[i]);
+                if (tok_ok) store4<TOut>(Otok + (long)hh * D + 16 * dt + 4 * q4, o);
+            }
+        }
+    } else {
+        float4 Kc[2][D / 16];
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int u = 0; u < D / 16; ++u)
+                Kc[T][u] = *reinterpret_cast<const float4 *>(
+                    &Klds[(kBlk * wave + 16 * T + c16) * KS + 16 * u + 4 * q4]);
+        for (int hh = 0; hh < group; ++hh) {
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+            for (int u = 0; u < D / 16; ++u) {
+                float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (tok_ok) qv = *reinterpret_cast<const float4 *>(Qtok + (long)hh * D + 16 * u + 4 * q4);
+                s0 = mfma_f32_16x16x4(Kc[0][u].x, qv.x, s0);
+                s0 = mfma_f32_16x16x4(Kc[0][u].y, qv.y, s0);
+                s0 = mfma_f32_16x16x4(Kc[0][u].z, qv.z, s0);
+                s0 = mfma_f32_16x16x4(Kc[0][u].w, qv.w, s0);
+                s1 = mfma_f32_16x16x4(Kc[1][u].x, qv.x, s1);
+                s1 = mfma_f32_16x16x4(Kc[1][u].y, qv.y, s1);
+                s1 = mfma_f32_16x16x4(Kc[1][u].z, qv.z, s1);
+                s1 = mfma_f32_16x16x4(Kc[1][u].w, qv.w, s1);
+            }
+            float x[8], m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (mask >> i & 1) ? s0[i] * a.scale_log2e : -INFINITY;
+                x[4 + i] = (mask >> (4 + i) & 1) ? s1[i] * a.scale_log2e : -INFINITY;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, x[i]);
+            m = max_over_groups(m);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = (mask >> i & 1) ? exp2f(x[i] - m) : 0.f;
+                sum += x[i];
+            }
+            sum = sum_over_groups(sum);
+            const float inv = 1.f / sum;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] *= inv;
+            const float al = alpha[hh];
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                // k-step s: lane group q4 supplies key 4*q4 + s of tile s/4
+                const float *vr = &Vt[(16 * dt + c16) * VS + kBlk * wave + 4 * q4];
+                const float4 v0 = *reinterpret_cast<const float4 *>(vr);
+                const float4 v1 = *reinterpret_cast<const float4 *>(vr + 16);
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                o = mfma_f32_16x16x4(v0.x, x[0], o);
+                o = mfma_f32_16x16x4(v0.y, x[1], o);
+                o = mfma_f32_16x16x4(v0.z, x[2], o);
+                o = mfma_f32_16x16x4(v0.w, x[3], o);
+                o = mfma_f32_16x16x4(v1.x, x[4], o);
+                o = mfma_f32_16x16x4(v1.y, x[5], o);
+                o = mfma_f32_16x16x4(v1.z, x[6], o);
+                o = mfma_f32_16x16x4(v1.w, x[7], o);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = fmaf(al, Sc[dt][i], o[i]);
+                if (tok_ok) store4<TOut>(Otok + (long)hh * D + 16 * dt + 4 * q4, o);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_ring_handoff: last min(W, n) keys/values of a continued call -> ring slots
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__global__ __launch_bounds__(256) void k_ring_handoff(PrefillArgs a) {
+    const int bg = blockIdx.x;
+    const int b = bg / a.Hkv, G = bg % a.Hkv;
+    const int n = a.n, W = a.W, D = a.d;
+    const int p0 = max(0, a.pos0[b]);
+    const int first = max(0, n - W);
+    const long row_stride = (long)a.Hkv * D;
+    const TIn *Kbg = reinterpret_cast<const TIn *>(a.k) + ((long)b * n * a.Hkv + G) * D;
+    const TIn *Vbg = reinterpret_cast<const TIn *>(a.v) + ((long)b * n * a.Hkv + G) * D;
+    TIn *rk = reinterpret_cast<TIn *>(a.ring_k) + (long)bg * W * D;
+    TIn *rv = reinterpret_cast<TIn *>(a.ring_v) + (long)bg * W * D;
+    const int cnt = (n - first) * D;
+    for (int idx = threadIdx.x; idx < cnt; idx += 256) {
+        const int t = first + idx / D, e = idx % D;
+        const int slot = (p0 + t) % W;
+        rk[(long)slot * D + e] = Kbg[(long)t * row_stride + e];
+        rv[(long)slot * D + e] = Vbg[(long)t * row_stride + e];
+    }
+}
+
+template <typename TIn, typename TOut, int D>
+hipError_t launch_t(const PrefillArgs &a, hipStream_t stream, int parts) {
+    const unsigned tiles = (unsigned)(a.B * a.Hkv * a.ntiles);
+    if (parts & kPrefillScan) {
+        hipLaunchKernelGGL((k_ewma_agg<TIn, D>), dim3((tiles + 3) / 4), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(k_ewma_carry, dim3(a.B * a.Hkv * (D / kCarryCols)), dim3(1024), 0, stream, a);
+    }
+    if (parts & kPrefillAttend) {
+        hipLaunchKernelGGL((k_window_attn<TIn, TOut, D>), dim3(tiles), dim3(256), 0, stream, a);
+        if (a.pos0 && a.ring_k)
+            hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_d(const PrefillArgs &a, hipStream_t stream, int parts) {
+    return a.d == 128 ? launch_t<TIn, TOut, 128>(a, stream, parts)
+                      : launch_t<TIn, TOut, 64>(a, stream, parts);
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int B, int n, int Hkv, int d) {
+    const size_t nt = (size_t)((n + kTile - 1) / kTile);
+    return (size_t)B * Hkv * nt * d * sizeof(float) * 6;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int parts) {
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_d<__bf16, __bf16>(a, stream, parts)
+                          : launch_d<__bf16, float>(a, stream, parts);
+    return a.out_bf16 ? launch_d<float, __bf16>(a, stream, parts) : launch_d<float, float>(a, stream, parts);
+}
+
+}  // namespace sfa

@@ -1,0 +1,95 @@
+// sfa_common.h -- internal helpers shared by the gfx950 SFA kernels.
+//
+// Wave64 lane layouts used throughout:
+//   MFMA 16x16 outputs: lane l holds D[4*(l/16) + i][l%16], i = 0..3.
+//   MFMA operands: lane l supplies row/column l%16 and a k-group l/16.  The
+//   kernels rely only on A and B using the SAME k assignment, which the
+//   instruction guarantees, so any consistent k permutation gives the exact
+//   same sum over k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxWindow = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// round-to-nearest-even (hardware v_cvt_pk_bf16_f32)
+__device__ __forceinline__ __bf16 f32_to_bf16(float x) { return (__bf16)x; }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// ---- cross-lane reductions over the four 16-lane groups (l ^ 16, l ^ 32) ----
+__device__ __forceinline__ float max_over_groups(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// ---- typed element access -------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float *p) { return *p; }
+    __device__ __forceinline__ static void store(float *p, float x) { *p = x; }
+};
+template <> struct Elem<__bf16> {
+    __device__ __forceinline__ static float load(const __bf16 *p) { return (float)*p; }
+    __device__ __forceinline__ static void store(__bf16 *p, float x) { *p = (__bf16)x; }
+};
+
+// load two consecutive elements as fp32
+__device__ __forceinline__ void load2(const float *p, float &a, float &b) {
+    float2 v = *reinterpret_cast<const float2 *>(p);
+    a = v.x; b = v.y;
+}
+__device__ __forceinline__ void load2(const __bf16 *p, float &a, float &b) {
+    uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+    a = bf16_lo(w); b = bf16_hi(w);
+}
+__device__ __forceinline__ void store2(float *p, float a, float b) {
+    *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+}
+__device__ __forceinline__ void store2(__bf16 *p, float a, float b) {
+    *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(a, b);
+}
+
+// MFMA wrappers
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// split fp32 x into bf16 hi + bf16 lo with x ~= hi + lo (relative error ~2^-17)
+__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+}  // namespace sfa

@@ -1,0 +1,89 @@
+// sfa_internal.h -- launch interfaces between the C ABI (sfa_api.cpp) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sfa {
+
+struct DecodeArgs {
+    const void *q, *k_new, *v_new;
+    void *ring_k, *ring_v;
+    float *state;
+    const int32_t *pos;
+    const float *gamma, *alpha;
+    void *out;
+    int L, B, Hq, Hkv, d, W, group;
+    float scale_log2e;
+    int in_bf16, out_bf16;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+// prefill tiling: 64-token tiles, four 16-token wave blocks per tile
+constexpr int kTile = 64;
+constexpr int kBlk = 16;
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *gamma, *alpha;
+    void *out;
+    void *ring_k, *ring_v;
+    float *state;
+    const int32_t *pos0;
+    int B, n, Hq, Hkv, d, W, group, ntiles;
+    float scale_log2e;
+    int in_bf16, out_bf16;
+    // workspace carve-up (fp32)
+    float *agg16;  // [B*Hkv][ntiles][4][d]  local EWMA aggregate of each 16-token block
+    float *agg64;  // [B*Hkv][ntiles][d]     local EWMA aggregate of each 64-token tile
+    float *carry;  // [B*Hkv][ntiles][d]     S just before each tile
+};
+size_t prefill_workspace_bytes(int B, int n, int Hkv, int d);
+constexpr int kPrefillScan = 1, kPrefillAttend = 2;
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int parts);
+
+struct EnhanceArgs {
+    const void *attn;
+    void *out;
+    float *ring, *field;
+    const float *pool;
+    long long pool_stride;
+    float *enhancement;
+    int L, layer0, n_layers, T, H, t0, R, n_slots, ntiles, n_pool_layers;
+    float alpha_base, cross_decay, ema_gamma, inv_temp_log2e, clip;
+    int in_bf16, out_bf16;
+    // workspace carve-up
+    float *agg64;           // [L][ntiles][H]   EMA of each 64-token tile from zero
+    float *carry;           // [L][ntiles][H]   field just before each tile
+    float *slot_norm;       // [n_pool_layers][64]
+    uint16_t *poolA;        // [n_pool_layers][H/32][4][2][64][8] bf16 hi/lo, cosine operand
+    uint16_t *poolT;        // [n_pool_layers][H/16][2][2][64][8] bf16 hi/lo, semantic operand
+};
+size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers);
+hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream);
+
+// XCD-aware block remap: consecutive logical indices land on the same XCD
+// (hardware dispatches workgroups round-robin over the 8 XCDs of an MI355X).
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+    constexpr int kXcd = 8;
+    const int xcd = bid % kXcd;
+    const int idx = bid / kXcd;
+    const int per = nblk / kXcd;
+    const int rem = nblk % kXcd;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// γ^k for small non-negative integer k (exponentiation by squaring, fp32)
+__device__ __forceinline__ float powi(float g, int k) {
+    float r = 1.0f;
+    while (k > 0) {
+        if (k & 1) r *= g;
+        g *= g;
+        k >>= 1;
+    }
+    return r;
+}
+
+}  // namespace sfa

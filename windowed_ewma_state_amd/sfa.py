@@ -1,0 +1,183 @@
+"""Thin Python binding of libsfa.so: torch tensors in, the C ABI underneath.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind include/sfa.h; PyTorch provides device memory and the current
+stream.  Names and argument meanings follow the C entry points
+(sfa_prefill, sfa_decode_step, sfa_enhance).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.SFA_F32, torch.bfloat16: _lib.SFA_BF16}
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _dev(t, name, dtype=None, shape=None, device=None):
+    """Validate a device tensor and return its pointer (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _vec(x, n, device, name):
+    """Per-head parameter as an fp32 device vector of length n (scalars broadcast)."""
+    if isinstance(x, torch.Tensor):
+        x = x.to(device=device, dtype=torch.float32)
+        if x.numel() == 1:
+            x = x.reshape(1).expand(n)
+        x = x.contiguous()
+        if tuple(x.shape) != (n,) and x.numel() == n:
+            x = x.reshape(n)
+        if x.numel() != n:
+            raise ValueError(f"{name} must have {n} elements")
+        return x
+    return torch.full((n,), float(x), dtype=torch.float32, device=device)
+
+
+def prefill_workspace_size(B: int, n: int, Hkv: int, d: int) -> int:
+    return int(_lib.lib().sfa_prefill_workspace_size(B, n, Hkv, d))
+
+
+def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=None,
+            out_dtype=None, ring_k=None, ring_v=None, state=None, pos0=None, workspace=None,
+            stream=None, parts: int | None = None):
+    """sfa_prefill: q [B,n,Hq,d], k/v [B,n,Hkv,d] (BNHD, bf16 or fp32).
+
+    gamma: [Hkv] (or scalar) decay per KV head; alpha: [Hq] (or scalar).
+    Returns (out, ring_k, ring_v, state).  ring_k/ring_v [B,Hkv,W,d] and
+    state [B,Hkv,d] fp32 are allocated when not given; pass them (and pos0 [B]
+    int32) to continue an existing cache.  `parts` (SFA_PREFILL_SCAN = 1,
+    SFA_PREFILL_ATTEND = 2) selects sfa_prefill_part; the two parts must share
+    every argument, including the workspace.
+    """
+    B, n, Hq, d = q.shape
+    Hkv = k.shape[2]
+    dev = q.device
+    W = int(window)
+    in_code = _dtype_code(q, "q")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, n, Hq, d), dtype=out_dtype, device=dev)
+    out_code = _dtype_code(out, "out")
+    if ring_k is None and pos0 is None:
+        ring_k = torch.zeros((B, Hkv, W, d), dtype=q.dtype, device=dev)
+        ring_v = torch.zeros((B, Hkv, W, d), dtype=q.dtype, device=dev)
+    if state is None and pos0 is None:
+        state = torch.zeros((B, Hkv, d), dtype=torch.float32, device=dev)
+    g = _vec(gamma, Hkv, dev, "gamma")
+    a = _vec(alpha, Hq, dev, "alpha")
+    need = prefill_workspace_size(B, n, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    L = _lib.lib()
+    fn = L.sfa_prefill if parts is None else (lambda *a_: L.sfa_prefill_part(int(parts), *a_))
+    st = fn(
+        _dev(q, "q", q.dtype, (B, n, Hq, d), dev), _dev(k, "k", q.dtype, (B, n, Hkv, d), dev),
+        _dev(v, "v", q.dtype, (B, n, Hkv, d), dev), _dev(g, "gamma"), _dev(a, "alpha"),
+        _dev(out, "out", None, (B, n, Hq, d), dev),
+        _dev(ring_k, "ring_k", q.dtype, (B, Hkv, W, d), dev),
+        _dev(ring_v, "ring_v", q.dtype, (B, Hkv, W, d), dev),
+        _dev(state, "state", torch.float32, (B, Hkv, d), dev),
+        _dev(pos0, "pos0", torch.int32, (B,), dev),
+        B, n, Hq, Hkv, d, W, float(scale), in_code, out_code,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream, dev))
+    _lib.check(st, "sfa_prefill" if parts is None else "sfa_prefill_part")
+    return out, ring_k, ring_v, state
+
+
+def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, *, scale: float = 0.0,
+                out=None, out_dtype=None, stream=None):
+    """sfa_decode_step over L layers: q [L,B,Hq,d], k_new/v_new [L,B,Hkv,d],
+    ring_k/ring_v [L,B,Hkv,W,d] and state [L,B,Hkv,d] fp32 updated in place,
+    pos [B] int32, gamma [L,Hkv], alpha [L,Hq].  Returns out [L,B,Hq,d]."""
+    L, B, Hq, d = q.shape
+    Hkv = k_new.shape[2]
+    W = ring_k.shape[3]
+    dev = q.device
+    in_code = _dtype_code(q, "q")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((L, B, Hq, d), dtype=out_dtype, device=dev)
+    out_code = _dtype_code(out, "out")
+    g = _vec(gamma, L * Hkv, dev, "gamma")
+    a = _vec(alpha, L * Hq, dev, "alpha")
+    st = _lib.lib().sfa_decode_step(
+        _dev(q, "q", q.dtype, (L, B, Hq, d), dev), _dev(k_new, "k_new", q.dtype, (L, B, Hkv, d), dev),
+        _dev(v_new, "v_new", q.dtype, (L, B, Hkv, d), dev),
+        _dev(ring_k, "ring_k", q.dtype, (L, B, Hkv, W, d), dev),
+        _dev(ring_v, "ring_v", q.dtype, (L, B, Hkv, W, d), dev),
+        _dev(state, "state", torch.float32, (L, B, Hkv, d), dev),
+        _dev(pos, "pos", torch.int32, (B,), dev), _dev(g, "gamma"), _dev(a, "alpha"),
+        _dev(out, "out", None, (L, B, Hq, d), dev),
+        L, B, Hq, Hkv, d, W, float(scale), in_code, out_code, _stream(stream, dev))
+    _lib.check(st, "sfa_decode_step")
+    return out
+
+
+def enhance_workspace_size(L: int, T: int, H: int) -> int:
+    return int(_lib.lib().sfa_enhance_workspace_size(L, T, H))
+
+
+def enhance(attn, pool, ring, field, *, layer0: int = 0, n_layers: int | None = None, t0: int = 0,
+            alpha_base: float = 0.1, cross_decay: float = 0.8, ema_gamma: float = 0.98,
+            temperature: float = 0.07, clip: float = 0.5, shared_pool: bool = False, out=None,
+            out_dtype=None, enhancement=None, workspace=None, stream=None):
+    """sfa_enhance: attn [L,T,H]; pool [L,n_slots,H] fp32 (or [n_slots,H] with
+    shared_pool=True); ring [L,R,H] and field [L,H] fp32 updated in place.
+    Returns (out, enhancement) -- enhancement is None unless a buffer is given."""
+    L, T, H = attn.shape
+    R = ring.shape[1]
+    dev = attn.device
+    in_code = _dtype_code(attn, "attn")
+    out_dtype = attn.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((L, T, H), dtype=out_dtype, device=dev)
+    out_code = _dtype_code(out, "out")
+    if shared_pool:
+        n_slots = pool.shape[0]
+        stride = 0
+        pshape = (n_slots, H)
+    else:
+        n_slots = pool.shape[1]
+        stride = n_slots * H
+        pshape = (L, n_slots, H)
+    nl = layer0 + L if n_layers is None else n_layers
+    need = enhance_workspace_size(L, T, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = _lib.lib().sfa_enhance(
+        _dev(attn, "attn", None, (L, T, H), dev), _dev(out, "out", None, (L, T, H), dev),
+        _dev(ring, "ring", torch.float32, (L, R, H), dev), _dev(field, "field", torch.float32, (L, H), dev),
+        _dev(pool, "pool", torch.float32, pshape, dev), stride,
+        _dev(enhancement, "enhancement", torch.float32, (L, T, H), dev),
+        L, layer0, nl, T, H, t0, float(alpha_base), float(cross_decay), float(ema_gamma),
+        float(temperature), float(clip), R, n_slots, in_code, out_code,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream, dev))
+    _lib.check(st, "sfa_enhance")
+    return out, enhancement

@@ -12,17 +12,19 @@
 // slots, clip 0.5) are the SFA_Config of page "Signal Field Attention (SFA)".
 //
 // Launches:
-//   k_pool_prep    pool -> bf16 hi/lo in the two MFMA operand orders, slot norms.
+//   k_pool_prep    pool -> bf16 hi/lo in the two MFMA operand orders.
+//   k_slot_norm    |s| of every pool slot.
 //   k_field_agg    EMA of each 64-token tile from zero (a thread per 16-byte column chunk).
 //   k_field_carry  field before each tile (exclusive scan), final field.
-//   k_enhance      one wave per (layer, 64-token tile), four tiles per
-//                  workgroup, XCD-aware order:
-//                    cosine scores  C^T = pool · a^T   (MFMA, pool operand
-//                                   reused by the 4 token groups of 16),
-//                    softmax over the 64 slots in registers,
-//                    per 64-column chunk: ring-mean + field scan into LDS,
-//                    semantic sum   sem^T = pool^T · w^T (MFMA), clip, scale,
-//                                   add, store.
+//   k_enhance      one workgroup per (layer, 64-token tile), XCD-aware order;
+//                  wave w owns a quarter of the hidden dimension:
+//                    cosine scores  C^T = pool · a^T over its quarter (MFMA,
+//                                   each pool operand reused by 4 token
+//                                   groups of 16), partials summed via LDS,
+//                    softmax over the 64 slots (wave w: token group w),
+//                    per 64-column chunk of its quarter and 16-token group:
+//                    ring-mean + field scan into LDS, semantic sum
+//                    sem^T = pool^T · w^T (MFMA), clip, scale, add, store.
 //   k_ring_out     last min(R, T) attention rows -> ring (after all reads).
 // Precision: the fp32 pool and the softmax weights enter the MFMAs as bf16
 // hi + lo pairs (x = hi + lo to ~2^-17 relative); bf16 attention values are
@@ -38,7 +40,6 @@ namespace {
 
 constexpr int kSlots = 64;
 constexpr int kCols = 64;          // columns per epilogue chunk (one per lane)
-constexpr int kTilesPerBlock = 4;  // waves (64-token tiles) per workgroup
 constexpr int kOpElems = 64 * 8;   // one MFMA operand (64 lanes x 8 bf16)
 
 __device__ __forceinline__ float alpha_layer(float base, float decay, int layer, int n_layers) {
@@ -72,7 +73,6 @@ __device__ __forceinline__ bf16x8 get8(const uint16_t *src) {
 //   poolT[pl][xg][ks][hl][lane][8]: x = 16xg + lane%16,
 //       slot = 32ks + (e<4 ? 4(lane/16)+e : 16+4(lane/16)+e-4)
 //       (A operand of the semantic sum, k = slot)
-//   slot_norm[pl][slot] = max(|s|, 1e-12)
 // One workgroup per (pool layer, 32-column step); 256 threads = 4 j x 64 lanes.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pool_prep(EnhanceArgs a) {
@@ -111,18 +111,6 @@ __global__ __launch_bounds__(256) void k_pool_prep(EnhanceArgs a) {
             put8(dst, hi);
             put8(dst + kOpElems, lo);
         }
-    }
-    if (ks == 0) {  // slot norms: 4 threads per slot
-        const int slot = threadIdx.x / 4, part = threadIdx.x % 4;
-        float ss = 0.f;
-        if (slot < a.n_slots)
-            for (int x = part; x < a.H; x += 4) {
-                const float v = P[(long)slot * a.H + x];
-                ss = fmaf(v, v, ss);
-            }
-        ss += __shfl_xor(ss, 1);
-        ss += __shfl_xor(ss, 2);
-        if (part == 0) a.slot_norm[pl * kSlots + slot] = fmaxf(sqrtf(ss), 1e-12f);
     }
 }
 
@@ -268,17 +256,27 @@ __device__ __forceinline__ void store4o<__bf16>(__bf16 *p, f32x4 v) {
 }
 
 template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void k_enhance(EnhanceArgs a) {
-    constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split everything
+__global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
+    constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split a as well
     constexpr int XS = kCols + 4;                                // LDS row stride (floats)
-    __shared__ __attribute__((aligned(16))) float Xl[kTilesPerBlock][kTile * XS];  // rm/R + 0.5·field
+    // phase 1 exchange (cosine partials) aliases the phase 2 buffers (scan output)
+    struct Phase1 {
+        f32x4 cp[4][2][4][64];  // [wave][slot tile in round][token group][lane]
+        float sq[4][4][64];     // [wave][token group][lane]
+    };
+    struct Phase2 {
+        float X[4][kBlk * XS];  // per wave: ring mean/R + 0.5·field for 16 tokens x 64 columns
+        float A[4][kBlk * XS];  // per wave: the attention values of the same block
+    };
+    __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(Phase1) > sizeof(Phase2)
+                                                               ? sizeof(Phase1) : sizeof(Phase2)];
+    __shared__ __attribute__((aligned(16))) u32x4 Wx[4][2][2][64];  // [tg][ks][hi/lo][lane]
+    Phase1 &p1 = *reinterpret_cast<Phase1 *>(smem);
+    Phase2 &p2 = *reinterpret_cast<Phase2 *>(smem);
 
-    const int groups = (a.ntiles + kTilesPerBlock - 1) / kTilesPerBlock;
-    const int lid = xcd_remap(blockIdx.x, a.L * groups);
-    const int l = lid / groups;
+    const int lid = xcd_remap(blockIdx.x, a.L * a.ntiles);
+    const int l = lid / a.ntiles, tile = lid % a.ntiles;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int tile = (lid % groups) * kTilesPerBlock + wave;
-    if (tile >= a.ntiles) return;  // wave-uniform; the kernel has no workgroup barrier
     const int q4 = lane >> 4, c16 = lane & 15;
     const int H = a.H, T = a.T, R = a.R;
     const int tb = tile * kTile;
@@ -291,7 +289,9 @@ __global__ __launch_bounds__(256) void k_enhance(EnhanceArgs a) {
     const float al = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
     const int nj = (a.n_slots + 15) / 16;
 
-    // ---- (1) cosine scores: lane holds C^T[slot 16j+4q4+i][token tb+16tg+c16] ----
+    // ---- (1) partial cosine scores over this wave's quarter of the hidden dim ----
+    // lane holds C^T[slot 16j+4q4+i][token tb+16tg+c16] for its k-steps
+    const int ks0 = wave * ksteps / 4, ks1 = (wave + 1) * ksteps / 4;
     f32x4 C[4][4];
     float sq[4];
 #pragma unroll
@@ -308,41 +308,63 @@ __global__ __launch_bounds__(256) void k_enhance(EnhanceArgs a) {
         tok_ok[tg] = t < T;
         arow[tg] = Ag + (long)(tok_ok[tg] ? t : tb) * H + 8 * q4;
     }
-    for (int ks = 0; ks < ksteps; ++ks) {
+    for (int ks = ks0; ks < ks1; ++ks) {
         bf16x8 bh[4], bl[4];
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg) load_a8<TIn>(arow[tg] + 32 * ks, bh[tg], bl[tg], sq[tg]);
+        for (int tg = 0; tg < 4; ++tg) {
+            load_a8<TIn>(arow[tg] + 32 * ks, bh[tg], bl[tg], sq[tg]);
+            if (!tok_ok[tg]) bh[tg] = bl[tg] = bf16x8{};
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j < nj) {
                 const uint16_t *op = poolA + (((long)ks * 4 + j) * 2) * kOpElems;
-                const bf16x8 ph = get8(op);
+                const bf16x8 ph = get8(op), plo = get8(op + kOpElems);
 #pragma unroll
-                for (int tg = 0; tg < 4; ++tg) C[j][tg] = mfma_bf16_16x16x32(ph, bh[tg], C[j][tg]);
-                const bf16x8 plo = get8(op + kOpElems);
-#pragma unroll
-                for (int tg = 0; tg < 4; ++tg) C[j][tg] = mfma_bf16_16x16x32(plo, bh[tg], C[j][tg]);
-                if constexpr (kPrecise) {
-#pragma unroll
-                    for (int tg = 0; tg < 4; ++tg) C[j][tg] = mfma_bf16_16x16x32(ph, bl[tg], C[j][tg]);
+                for (int tg = 0; tg < 4; ++tg) {
+                    C[j][tg] = mfma_bf16_16x16x32(ph, bh[tg], C[j][tg]);
+                    C[j][tg] = mfma_bf16_16x16x32(plo, bh[tg], C[j][tg]);
+                    if constexpr (kPrecise) C[j][tg] = mfma_bf16_16x16x32(ph, bl[tg], C[j][tg]);
                 }
             }
         }
     }
-
-    // ---- (2) softmax over slots; w as the B operand of the semantic sum -----------
-    // k-step ks of the semantic sum holds slot tiles 2ks (e<4) and 2ks+1 (e>=4)
-    bf16x8 Wh[4][2], Wl[4][2];
+    // ---- (2) reduce the four partials: wave w ends with token group tg = w -------
+    f32x4 Cw[4];
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-        const float inv_na = 1.f / fmaxf(sqrtf(sum_over_groups(sq[tg])), 1e-12f);
+    for (int tg = 0; tg < 4; ++tg) p1.sq[wave][tg][lane] = sq[tg];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) p1.cp[wave][jj][tg][lane] = C[2 * r + jj][tg];
+        __syncthreads();
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            f32x4 acc = p1.cp[0][jj][wave][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < 4; ++w2) {
+                const f32x4 o = p1.cp[w2][jj][wave][lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += o[i];
+            }
+            Cw[2 * r + jj] = acc;
+        }
+        __syncthreads();
+    }
+    float sqw = p1.sq[0][wave][lane] + p1.sq[1][wave][lane] + p1.sq[2][wave][lane] + p1.sq[3][wave][lane];
+
+    // ---- (3) softmax over slots for token group tg = wave ------------------------
+    {
+        const float inv_na = 1.f / fmaxf(sqrtf(sum_over_groups(sqw)), 1e-12f);
         float w[16], m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int slot = 16 * j + 4 * q4 + i;
-                w[4 * j + i] = slot < a.n_slots ? C[j][tg][i] * inv_na / snorm[slot] * a.inv_temp_log2e
+                w[4 * j + i] = slot < a.n_slots ? Cw[j][i] * inv_na / snorm[slot] * a.inv_temp_log2e
                                                 : -INFINITY;
                 m = fmaxf(m, w[4 * j + i]);
             }
@@ -354,34 +376,57 @@ __global__ __launch_bounds__(256) void k_enhance(EnhanceArgs a) {
             sum += w[k];
         }
         const float inv = 1.f / sum_over_groups(sum);
+        // B operand of the semantic sum: k-step ks holds slot tiles 2ks (e<4), 2ks+1 (e>=4)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 h8, l8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 __bf16 h, lo_;
                 split_bf16(w[4 * (2 * ks + (e >> 2)) + (e & 3)] * inv, h, lo_);
-                Wh[tg][ks][e] = h;
-                Wl[tg][ks][e] = lo_;
+                h8[e] = h;
+                l8[e] = lo_;
             }
+            Wx[wave][ks][0][lane] = __builtin_bit_cast(u32x4, h8);
+            Wx[wave][ks][1][lane] = __builtin_bit_cast(u32x4, l8);
+        }
     }
+    __syncthreads();
 
-    // ---- (3) per 64-column chunk: ring mean + field scan, semantic sum, epilogue ---
+    // ---- (4) this wave's column chunks: scan, semantic sum, epilogue --------------
     const float g = a.ema_gamma;
     const float invR = 1.f / (float)R;
     const int len = min(kTile, T - tb);
     const float *ringl = a.ring + (long)l * R * H;
+    const int ring0 = a.t0 % R;   // slot of relative token 0
+    const bool reach_ring = tb < R;  // only the first tile looks back before token 0
     const float *carry = a.carry + ((long)l * a.ntiles + tile) * H;
-    float *Xw = Xl[wave];
+    float *Xw = p2.X[wave];
+    float *Aw = p2.A[wave];
     TOut *Og = reinterpret_cast<TOut *>(a.out) + (long)l * T * H;
     float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
+    const int nch = H / kCols;
+    const int ch0 = wave * nch / 4, ch1 = (wave + 1) * nch / 4;
 
-    for (int xc = 0; xc < H; xc += kCols) {
+    for (int ch = ch0; ch < ch1; ++ch) {
+        const int xc = ch * kCols;
         const int x = xc + lane;
-        // value of relative token t at column x (t >= -R: the carried ring)
+        // the chunk's semantic-sum A operands (4 column tiles x k-steps x hi/lo),
+        // shared by its four token groups; issued before the scan's loads
+        bf16x8 pt[kCols / 16][4];
+#pragma unroll
+        for (int xt = 0; xt < kCols / 16; ++xt)
+#pragma unroll
+            for (int o = 0; o < 4; ++o) pt[xt][o] = get8(poolT + ((long)(xc / 16 + xt) * 4 + o) * kOpElems);
+        // value of relative token t at column x; -R <= t < 0 reads the carried
+        // ring, slot (t0 + t) mod R = ring0 + t (+R when negative)
+        const TIn *Acol = Ag + x;
         auto val = [&](int t) -> float {
-            if (t >= 0) return t < T ? Elem<TIn>::load(Ag + (long)t * H + x) : 0.f;
-            const int slot = (int)((((long)a.t0 + t) % R + R) % R);
-            return ringl[(long)slot * H + x];
+            if (reach_ring && t < 0) {
+                const int slot = ring0 + t < 0 ? ring0 + t + R : ring0 + t;
+                return ringl[(long)slot * H + x];
+            }
+            return t < T ? Elem<TIn>::load(Acol + (long)t * H) : 0.f;
         };
         // ring sum of tokens tb-R .. tb-1, then slide: + token j, - token j-R
         float rs = 0.f;
@@ -393,10 +438,18 @@ __global__ __launch_bounds__(256) void k_enhance(EnhanceArgs a) {
             for (int k = 0; k < kBlk; ++k) rs += pre[k];
         }
         float F = carry[x];
-        for (int j0 = 0; j0 < len; j0 += kBlk) {
+        for (int tg = 0; tg < 4; ++tg) {
+            const int j0 = 16 * tg;
+            if (j0 >= len) break;  // wave-uniform
+            // this token group's softmax weights (B operands), from LDS
+            const bf16x8 wh0 = __builtin_bit_cast(bf16x8, Wx[tg][0][0][lane]);
+            const bf16x8 wl0 = __builtin_bit_cast(bf16x8, Wx[tg][0][1][lane]);
+            const bf16x8 wh1 = __builtin_bit_cast(bf16x8, Wx[tg][1][0][lane]);
+            const bf16x8 wl1 = __builtin_bit_cast(bf16x8, Wx[tg][1][1][lane]);
+            const bool tok_ok_g = tb + j0 + c16 < T;
             float cur[kBlk], old[kBlk];
 #pragma unroll
-            for (int j = 0; j < kBlk; ++j) {  // the batch's loads are all in flight together
+            for (int j = 0; j < kBlk; ++j) {  // the block's loads are all in flight together
                 const bool ok = j0 + j < len;
                 cur[j] = ok ? val(tb + j0 + j) : 0.f;
                 old[j] = ok ? val(tb + j0 + j - R) : 0.f;
@@ -406,77 +459,84 @@ __global__ __launch_bounds__(256) void k_enhance(EnhanceArgs a) {
                 if (j0 + j < len) {
                     rs += cur[j] - old[j];
                     F = g * F + (1.f - g) * cur[j];
-                    Xw[(j0 + j) * XS + lane] = rs * invR + 0.5f * F;
                 }
+                Xw[j * XS + lane] = rs * invR + 0.5f * F;
+                Aw[j * XS + lane] = cur[j];
             }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int xt = 0; xt < kCols / 16; ++xt) {
-            const int xg = xc / 16 + xt;
-            const uint16_t *op = poolT + ((long)xg * 2 * 2) * kOpElems;
-            const bf16x8 th0 = get8(op), th1 = get8(op + 2 * kOpElems);
-            const bf16x8 tl0 = get8(op + kOpElems), tl1 = get8(op + 3 * kOpElems);
-            const int xl = 16 * xt + 4 * q4;
-#pragma unroll
-            for (int tg = 0; tg < 4; ++tg) {
-                f32x4 s = {0.f, 0.f, 0.f, 0.f};
-                s = mfma_bf16_16x16x32(th0, Wh[tg][0], s);
-                s = mfma_bf16_16x16x32(th0, Wl[tg][0], s);
-                s = mfma_bf16_16x16x32(th1, Wh[tg][1], s);
-                s = mfma_bf16_16x16x32(th1, Wl[tg][1], s);
-                s = mfma_bf16_16x16x32(tl0, Wh[tg][0], s);
-                s = mfma_bf16_16x16x32(tl1, Wh[tg][1], s);
-                // lane: sem[x = xc + xl + i][token tb + 16tg + c16]
-                const int jt = 16 * tg + c16;
-                if (tok_ok[tg]) {
-                    const f32x4 X4 = *reinterpret_cast<const f32x4 *>(&Xw[jt * XS + xl]);
-                    const long off = (long)(tb + jt) * H + xc + xl;
-                    const f32x4 A4 = load4f<TIn>(Ag + off);
+            for (int xt = 0; xt < kCols / 16; ++xt) {
+                const bf16x8 th0 = pt[xt][0], tl0 = pt[xt][1], th1 = pt[xt][2], tl1 = pt[xt][3];
+                f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+                sm = mfma_bf16_16x16x32(th0, wh0, sm);
+                sm = mfma_bf16_16x16x32(th0, wl0, sm);
+                sm = mfma_bf16_16x16x32(tl0, wh0, sm);
+                sm = mfma_bf16_16x16x32(th1, wh1, sm);
+                sm = mfma_bf16_16x16x32(th1, wl1, sm);
+                sm = mfma_bf16_16x16x32(tl1, wh1, sm);
+                // lane: sem[x = xc + 16xt + 4q4 + i][token tb + j0 + c16]
+                const int xl = 16 * xt + 4 * q4;
+                if (tok_ok_g) {
+                    const f32x4 X4 = *reinterpret_cast<const f32x4 *>(&Xw[c16 * XS + xl]);
+                    const f32x4 A4 = *reinterpret_cast<const f32x4 *>(&Aw[c16 * XS + xl]);
                     f32x4 o, en;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = fminf(fmaxf(X4[i] + 0.5f * s[i], -a.clip), a.clip);
+                        const float e = fminf(fmaxf(X4[i] + 0.5f * sm[i], -a.clip), a.clip);
                         en[i] = al * e;
                         o[i] = A4[i] + en[i];
                     }
+                    const long off = (long)(tb + j0 + c16) * H + xc + xl;
                     store4o<TOut>(Og + off, o);
                     if (Eg) store4o<float>(Eg + off, en);
                 }
             }
+            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
-// last min(R, T) attention rows -> ring slots (t0 + t) mod R
+// last min(R, T) attention rows -> ring slots (t0 + t) mod R; one workgroup
+// per (layer, row)
 template <typename TIn>
 __global__ __launch_bounds__(256) void k_ring_out(EnhanceArgs a) {
-    const int l = blockIdx.x;
+    const int l = blockIdx.x / a.R, r = blockIdx.x % a.R;
     const int first = max(0, a.T - a.R);
-    const long cnt = (long)(a.T - first) * a.H;
-    const TIn *A = reinterpret_cast<const TIn *>(a.attn) + (long)l * a.T * a.H;
-    float *ring = a.ring + (long)l * a.R * a.H;
-    for (long idx = threadIdx.x; idx < cnt; idx += 256) {
-        const int t = first + (int)(idx / a.H);
-        const int x = (int)(idx % a.H);
-        ring[(long)(((long)a.t0 + t) % a.R) * a.H + x] = Elem<TIn>::load(A + (long)t * a.H + x);
+    const int t = first + r;
+    if (t >= a.T) return;
+    const TIn *A = reinterpret_cast<const TIn *>(a.attn) + ((long)l * a.T + t) * a.H;
+    float *dst = a.ring + ((long)l * a.R + (a.t0 % a.R + t % a.R) % a.R) * a.H;
+    for (int x = threadIdx.x; x < a.H; x += 256) dst[x] = Elem<TIn>::load(A + x);
+}
+
+// per-slot norms: one workgroup per (pool layer, slot)
+__global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
+    __shared__ float red[4];
+    const int pl = blockIdx.x / kSlots, slot = blockIdx.x % kSlots;
+    float ss = 0.f;
+    if (slot < a.n_slots) {
+        const float *P = a.pool + (long)pl * a.pool_stride + (long)slot * a.H;
+        for (int x = threadIdx.x; x < a.H; x += 256) ss = fmaf(P[x], P[x], ss);
     }
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        a.slot_norm[pl * kSlots + slot] = fmaxf(sqrtf(red[0] + red[1] + red[2] + red[3]), 1e-12f);
 }
 
 template <typename TIn, typename TOut>
 hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
-    const int groups = (a.ntiles + kTilesPerBlock - 1) / kTilesPerBlock;
     hipLaunchKernelGGL(k_pool_prep, dim3(a.n_pool_layers * (a.H / 32)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_slot_norm, dim3(a.n_pool_layers * kSlots), dim3(256), 0, stream, a);
     const int fchunks = a.H / (16 / (int)sizeof(TIn));
     hipLaunchKernelGGL((k_field_agg<TIn>), dim3(a.L * a.ntiles * ((fchunks + 255) / 256)), dim3(256), 0,
                        stream, a);
     hipLaunchKernelGGL(k_field_carry, dim3(a.L * ((a.H + 255) / 256)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((k_enhance<TIn, TOut>), dim3(a.L * groups), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((k_ring_out<TIn>), dim3(a.L), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_enhance<TIn, TOut>), dim3(a.L * a.ntiles), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_ring_out<TIn>), dim3(a.L * a.R), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

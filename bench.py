@@ -252,6 +252,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only", choices=["decode", "enhance"], default=None,
+                    help="run only this secondary measurement (for profiling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -263,6 +265,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.only:
+        print(json.dumps(run_decode() if args.only == "decode" else run_enhance()), flush=True)
         return
 
     pre = run_prefill(args)

@@ -234,8 +234,25 @@ __device__ __forceinline__ void store4<__bf16>(__bf16 *p, f32x4 v) {
     *reinterpret_cast<u32x2 *>(p) = w;
 }
 
+constexpr int kQSlots = 4;  // query heads whose Q operands are in flight together
+
+template <typename TOut>
+__device__ __forceinline__ void store8(TOut *p, const float *v);
+template <>
+__device__ __forceinline__ void store8<float>(float *p, const float *v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <>
+__device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float *v) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4 *>(p) = w;
+}
+
 template <typename TIn, typename TOut, int D>
-__global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     constexpr bool kBf16 = std::is_same<TIn, __bf16>::value;
     constexpr int EPL = D / kWave;
     constexpr int KS = D + Lds<TIn>::kpad;      // Klds row stride (elements)
@@ -259,6 +276,9 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
     const int t0 = tile * kTile;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
     const float gm = a.gamma[G];
+    const int tb = t0 + kBlk * wave;  // this wave's 16 tokens
+    const int tok = tb + c16;         // this lane's token in the MFMA layouts
+    const bool tok_ok = tok < n;
 
     const long row_stride = (long)a.Hkv * D;
     const TIn *Kbg = reinterpret_cast<const TIn *>(a.k) + ((long)b * n * a.Hkv + G) * D;
@@ -270,6 +290,31 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
     const bool write_ring = !cont && a.ring_k != nullptr;
     TIn *ringKw = write_ring ? reinterpret_cast<TIn *>(a.ring_k) + (long)bg * a.W * D : nullptr;
     TIn *ringVw = write_ring ? reinterpret_cast<TIn *>(a.ring_v) + (long)bg * a.W * D : nullptr;
+    const TIn *Qtok = reinterpret_cast<const TIn *>(a.q) + (((long)b * n + tok) * a.Hq + (long)G * group) * D;
+    TOut *Otok = reinterpret_cast<TOut *>(a.out) + (((long)b * n + tok) * a.Hq + (long)G * group) * D;
+
+    // ---- (0) the first heads' queries go out before the K/V staging ----------
+    // (B operands of the score MFMA: lane = token c16, 8 head-dim elements)
+    // Qc[i] holds the head h with h % kQSlots == i; it is refilled with head
+    // h + kQSlots as soon as head h is done, so four heads are always in flight.
+    // The loads are row-shaped: lane L reads the 16-byte chunk L % (D/8) of token
+    // L / (D/8) (+ 64/(D/8) per load) of the block, whole rows per instruction;
+    // an LDS tile turns them into MFMA operands.
+    constexpr int CPT = D / 8, TPI = 64 / CPT, QLD = kBlk / TPI;
+    const int rt = lane / CPT, rc = lane % CPT;
+    const TIn *Qrow = reinterpret_cast<const TIn *>(a.q) + (((long)b * n + tb + rt) * a.Hq + (long)G * group) * D + 8 * rc;
+    const long qtok_stride = (long)TPI * a.Hq * D;  // next token of this lane
+    u32x4 Qc[kQSlots][QLD];
+    if constexpr (kBf16) {
+#pragma unroll
+        for (int hh = 0; hh < kQSlots; ++hh)
+#pragma unroll
+            for (int j = 0; j < QLD; ++j) {
+                Qc[hh][j] = u32x4{0u, 0u, 0u, 0u};
+                if (hh < group && tb + rt + TPI * j < n)
+                    Qc[hh][j] = *reinterpret_cast<const u32x4 *>(Qrow + j * qtok_stride + (long)hh * D);
+            }
+    }
 
     // ---- (1) stage K rows (row-major) and V (transposed) ---------------------
     for (int idx = tid; idx < kRows * CPR; idx += 256) {
@@ -283,9 +328,11 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
             *reinterpret_cast<u32x4 *>(ringKw + (long)(t % W) * D + c * EPC) = val;
     }
     if constexpr (kBf16) {
-        // two keys per thread so each LDS write is one aligned dword
-        for (int idx = tid; idx < (kRows / 2) * CPR; idx += 256) {
-            const int m = idx / CPR, c = idx % CPR;
+        // two keys per thread so each LDS write is one aligned dword; key pairs
+        // vary fastest across lanes so a write instruction hits consecutive banks
+        constexpr int kPairs = kRows / 2;
+        for (int idx = tid; idx < kPairs * CPR; idx += 256) {
+            const int m = idx % kPairs, c = idx / kPairs;
             const int ta = t0 - kMaxWindow + 2 * m;
             const TIn *sa = kv_row(Vbg, row_stride, ringVr, ta, n, p0, W, D);
             const TIn *sb = kv_row(Vbg, row_stride, ringVr, ta + 1, n, p0, W, D);
@@ -308,7 +355,7 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
         }
     } else {
         for (int idx = tid; idx < kRows * CPR; idx += 256) {
-            const int r = idx / CPR, c = idx % CPR;
+            const int r = idx % kRows, c = idx / kRows;
             const int t = t0 - kMaxWindow + r;
             const TIn *src = kv_row(Vbg, row_stride, ringVr, t, n, p0, W, D);
             float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -341,7 +388,6 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
     __syncthreads();
 
     // ---- (3) EWMA through the block: S_t after token t's own eviction ---------
-    const int tb = t0 + kBlk * wave;
     float *Sw = Sb[wave];
 #pragma unroll
     for (int j = 0; j < kBlk; ++j) {
@@ -359,17 +405,9 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
     }
     __syncthreads();
 
-    // ---- (4) per-wave operand caches, shared by every head of the group ------
-    // key tiles: T0 = staged rows 16*wave + [0,16), T1 = 16*wave + 16 + [0,16)
-    // (keys tb-16 .. tb+15); row c16 of each tile is this lane's A row.
-    f32x4 Sc[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-        Sc[dt] = *reinterpret_cast<const f32x4 *>(&Sw[c16 * SS + 16 * dt + 4 * q4]);
-
-    // score-validity mask: element T*4+i is key (tb-16) + 16T + 4*q4 + i for token tb + c16
-    const int tok = tb + c16;
-    const bool tok_ok = tok < n;
+    // ---- (4) score-validity mask -------------------------------------------------
+    // element T*4+i is key (tb-16) + 16T + 4*q4 + i for token tb + c16; key tiles
+    // T0 = staged rows 16*wave + [0,16), T1 = 16*wave + 16 + [0,16)
     unsigned mask = 0;
 #pragma unroll
     for (int T = 0; T < 2; ++T)
@@ -378,9 +416,6 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
             const int kr = tb - kMaxWindow + 16 * T + 4 * q4 + i;
             if (kr <= tok && kr > tok - W && p0 + kr >= 0) mask |= 1u << (4 * T + i);
         }
-
-    const TIn *Qtok = reinterpret_cast<const TIn *>(a.q) + (((long)b * n + tok) * a.Hq + (long)G * group) * D;
-    TOut *Otok = reinterpret_cast<TOut *>(a.out) + (((long)b * n + tok) * a.Hq + (long)G * group) * D;
     const float *alpha = a.alpha + (long)G * group;
 
     if constexpr (kBf16) {
@@ -391,71 +426,116 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
             for (int st = 0; st < D / 32; ++st)
                 Kc[T][st] = *reinterpret_cast<const bf16x8 *>(
                     &Klds[(kBlk * wave + 16 * T + c16) * KS + 32 * st + 8 * q4]);
-        bf16x8 Vc[D / 16];
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            const TIn *vr = &Vt[(16 * dt + c16) * VS + kBlk * wave + 4 * q4];
-            const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
-            const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
-            u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-            Vc[dt] = __builtin_bit_cast(bf16x8, w);
-        }
+        const TIn *vrow0 = &Vt[kBlk * wave + 4 * q4];   // + d * VS: keys 4q4.. of T0, +16: of T1
+        const float *Srow = &Sw[c16 * SS + 8 * q4];     // S of token c16 at d = 32k + 8q4 + e
+        // bf16 outputs go through a per-wave [16 tokens][D] tile in the K staging
+        // area (free once every wave holds its K operands) so that each store
+        // instruction writes 4 whole rows of D bf16
+        constexpr bool kTileOut = std::is_same<TOut, __bf16>::value;
+        constexpr int OS = D + 8;  // Q / output tile row stride (bf16)
+        static_assert(4 * kBlk * OS * 2 <= (int)sizeof(Klds), "output tiles must fit the K area");
+        uint16_t *Ot = reinterpret_cast<uint16_t *>(Klds) + wave * kBlk * OS;
+        __syncthreads();
 
-        bf16x8 Qn[D / 32];
+        for (int h0 = 0; h0 < group; h0 += kQSlots) {
 #pragma unroll
-        for (int st = 0; st < D / 32; ++st) {
-            Qn[st] = bf16x8{};
-            if (tok_ok) Qn[st] = *reinterpret_cast<const bf16x8 *>(Qtok + 32 * st + 8 * q4);
-        }
-        for (int hh = 0; hh < group; ++hh) {
-            bf16x8 Qc[D / 32];
+            for (int hh = 0; hh < kQSlots; ++hh) {
+                const int h = h0 + hh;
+                if (h >= group) continue;  // unrolled: keeps Qc indices static
+                // row layout -> LDS tile -> B operands (lane: token c16, 8 elements)
 #pragma unroll
-            for (int st = 0; st < D / 32; ++st) Qc[st] = Qn[st];
-            if (hh + 1 < group) {  // prefetch the next head's queries
+                for (int j = 0; j < QLD; ++j)
+                    *reinterpret_cast<u32x4 *>(&Ot[(rt + TPI * j) * OS + 8 * rc]) = Qc[hh][j];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                bf16x8 Qh[D / 32];
 #pragma unroll
                 for (int st = 0; st < D / 32; ++st)
-                    if (tok_ok) Qn[st] = *reinterpret_cast<const bf16x8 *>(Qtok + (long)(hh + 1) * D + 32 * st + 8 * q4);
-            }
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+                    Qh[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&Ot[c16 * OS + 32 * st + 8 * q4]));
+                if (h + kQSlots < group) {  // refill the slot with head h + 4
 #pragma unroll
-            for (int st = 0; st < D / 32; ++st) {
-                s0 = mfma_bf16_16x16x32(Kc[0][st], Qc[st], s0);
-                s1 = mfma_bf16_16x16x32(Kc[1][st], Qc[st], s1);
-            }
-            float x[8], m = -INFINITY;
+                    for (int j = 0; j < QLD; ++j)
+                        if (tb + rt + TPI * j < n)
+                            Qc[hh][j] = *reinterpret_cast<const u32x4 *>(Qrow + j * qtok_stride + (long)(h + kQSlots) * D);
+                }
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = (mask >> i & 1) ? s0[i] * a.scale_log2e : -INFINITY;
-                x[4 + i] = (mask >> (4 + i) & 1) ? s1[i] * a.scale_log2e : -INFINITY;
-            }
+                for (int st = 0; st < D / 32; ++st) {
+                    s0 = mfma_bf16_16x16x32(Kc[0][st], Qh[st], s0);
+                    s1 = mfma_bf16_16x16x32(Kc[1][st], Qh[st], s1);
+                }
+                float x[8], m = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m = fmaxf(m, x[i]);
-            m = max_over_groups(m);
-            float sum = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    x[i] = (mask >> i & 1) ? s0[i] * a.scale_log2e : -INFINITY;
+                    x[4 + i] = (mask >> (4 + i) & 1) ? s1[i] * a.scale_log2e : -INFINITY;
+                }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                x[i] = (mask >> i & 1) ? exp2f(x[i] - m) : 0.f;
-                sum += x[i];
-            }
-            sum = sum_over_groups(sum);
-            const float inv = 1.f / sum;
-            bf16x8 Ph, Pl;
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, x[i]);
+                m = max_over_groups(m);
+                float sum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __bf16 h, l;
-                split_bf16(x[i] * inv, h, l);
-                Ph[i] = h;
-                Pl[i] = l;
-            }
-            const float al = alpha[hh];
+                for (int i = 0; i < 8; ++i) {
+                    x[i] = (mask >> i & 1) ? __builtin_amdgcn_exp2f(x[i] - m) : 0.f;
+                    sum += x[i];
+                }
+                sum = sum_over_groups(sum);
+                const float inv = 1.f / sum;
+                bf16x8 Ph, Pl;
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                f32x4 o = {0.f, 0.f, 0.f, 0.f};
-                o = mfma_bf16_16x16x32(Vc[dt], Ph, o);
-                o = mfma_bf16_16x16x32(Vc[dt], Pl, o);
+                for (int i = 0; i < 8; ++i) {
+                    __bf16 hi_, lo_;
+                    split_bf16(x[i] * inv, hi_, lo_);
+                    Ph[i] = hi_;
+                    Pl[i] = lo_;
+                }
+                const float al = alpha[h];
+                // PV in 16-row V^T tiles; row m of tile dt is head-dim element
+                // 32(dt/2) + 8(m/4) + 4(dt%2) + m%4, so after tiles 2k and 2k+1
+                // lane group q4 holds elements [32k + 8q4, +8) of its token and
+                // the four lanes of a token store 64 contiguous bytes
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = fmaf(al, Sc[dt][i], o[i]);
-                if (tok_ok) store4<TOut>(Otok + (long)hh * D + 16 * dt + 4 * q4, o);
+                for (int k = 0; k < D / 32; ++k) {
+                    float ov[8];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int drow = 32 * k + 8 * (c16 >> 2) + 4 * half + (c16 & 3);
+                        const TIn *vr = vrow0 + drow * VS;
+                        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
+                        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
+                        const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                        o = mfma_bf16_16x16x32(vop, Ph, o);
+                        o = mfma_bf16_16x16x32(vop, Pl, o);
+                        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(Srow + 32 * k + 4 * half);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ov[4 * half + i] = fmaf(al, s4[i], o[i]);
+                    }
+                    if constexpr (kTileOut) {
+                        u32x4 w;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
+                        *reinterpret_cast<u32x4 *>(&Ot[c16 * OS + 32 * k + 8 * q4]) = w;
+                    } else {
+                        if (tok_ok) store8<TOut>(Otok + (long)h * D + 32 * k + 8 * q4, ov);
+                    }
+                }
+                if constexpr (kTileOut) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    // lane L: token rt + TPI*j of the block, 16-byte chunk rc
+#pragma unroll
+                    for (int j = 0; j < kBlk / TPI; ++j) {
+                        const int tt = rt + TPI * j;
+                        const u32x4 w = *reinterpret_cast<const u32x4 *>(&Ot[tt * OS + 8 * rc]);
+                        if (tb + tt < n)
+                            *reinterpret_cast<u32x4 *>(reinterpret_cast<TOut *>(a.out) +
+                                (((long)b * n + tb + tt) * a.Hq + (long)G * group + h) * D + 8 * rc) = w;
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                }
             }
         }
     } else {
@@ -493,7 +573,7 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                x[i] = (mask >> i & 1) ? exp2f(x[i] - m) : 0.f;
+                x[i] = (mask >> i & 1) ? __builtin_amdgcn_exp2f(x[i] - m) : 0.f;
                 sum += x[i];
             }
             sum = sum_over_groups(sum);
@@ -516,8 +596,9 @@ __global__ __launch_bounds__(256) void k_window_attn(PrefillArgs a) {
                 o = mfma_f32_16x16x4(v1.y, x[5], o);
                 o = mfma_f32_16x16x4(v1.z, x[6], o);
                 o = mfma_f32_16x16x4(v1.w, x[7], o);
+                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&Sw[c16 * SS + 16 * dt + 4 * q4]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = fmaf(al, Sc[dt][i], o[i]);
+                for (int i = 0; i < 4; ++i) o[i] = fmaf(al, s4[i], o[i]);
                 if (tok_ok) store4<TOut>(Otok + (long)hh * D + 16 * dt + 4 * q4, o);
             }
         }

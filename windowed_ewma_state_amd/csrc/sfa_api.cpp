@@ -96,6 +96,7 @@ int sfa_decode_step(const void *q, const void *k_new, const void *v_new, void *r
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return SFA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return SFA_ERR_UNSUPPORTED;
     if (L == 0 || B == 0) return SFA_OK;
+    if ((long long)L * B * Hkv >= (1LL << 31) / 64) return SFA_ERR_INVALID_ARG;  // unit indices are 32-bit
     if (!q || !k_new || !v_new || !ring_k || !ring_v || !state || !pos || !gamma || !alpha || !out)
         return SFA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(ring_k, 16) ||

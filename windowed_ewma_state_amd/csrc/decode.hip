@@ -247,8 +247,8 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     for (int st = 0; st < D / 32; ++st) {
         u.kop[st] = bf16x8{};
         u.qop[st] = bf16x8{};
-        if (live && c16 < W) u.kop[st] = *reinterpret_cast<const bf16x8 *>(krow + 32 * st + 8 * q4);
-        if (live && c16 < group) u.qop[st] = *reinterpret_cast<const bf16x8 *>(qg + (long)c16 * D + 32 * st + 8 * q4);
+        if (live && c16 < W) u.kop[st] = __builtin_bit_cast(bf16x8, ld_stream(krow + 32 * st + 8 * q4));
+        if (live && c16 < group) u.qop[st] = __builtin_bit_cast(bf16x8, ld_stream(qg + (long)c16 * D + 32 * st + 8 * q4));
     }
     // V rows for the transpose: lane (m = lane % 8, c = lane / 8) holds slot rows
     // 2m and 2m+1 at 16-byte chunks c (+ 8 for d 128)
@@ -260,7 +260,7 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
         u.v[i] = u32x4{0u, 0u, 0u, 0u};
         if (live && r < nvalid) {
             const __bf16 *src = (r == s) ? vn : ringV + (long)r * D;
-            u.v[i] = *reinterpret_cast<const u32x4 *>(src + 8 * ch);
+            u.v[i] = ld_stream(src + 8 * ch);
         }
     }
     // far-field state, evicted key, new key/value (e-pair layout)
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
                         u32x4 w;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
-                        *reinterpret_cast<u32x4 *>(orow + 32 * k + 8 * q4) = w;
+                        st_stream(orow + 32 * k + 8 * q4, w);
                     }
                 }
             }

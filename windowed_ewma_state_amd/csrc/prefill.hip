@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             for (int j = 0; j < QLD; ++j) {
                 Qc[hh][j] = u32x4{0u, 0u, 0u, 0u};
                 if (hh < group && tb + rt + TPI * j < n)
-                    Qc[hh][j] = *reinterpret_cast<const u32x4 *>(Qrow + j * qtok_stride + (long)hh * D);
+                    Qc[hh][j] = ld_stream(Qrow + j * qtok_stride + (long)hh * D);
             }
     }
 
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
 #pragma unroll
                     for (int j = 0; j < QLD; ++j)
                         if (tb + rt + TPI * j < n)
-                            Qc[hh][j] = *reinterpret_cast<const u32x4 *>(Qrow + j * qtok_stride + (long)(h + kQSlots) * D);
+                            Qc[hh][j] = ld_stream(Qrow + j * qtok_stride + (long)(h + kQSlots) * D);
                 }
                 f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
@@ -531,8 +531,8 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
                         const int tt = rt + TPI * j;
                         const u32x4 w = *reinterpret_cast<const u32x4 *>(&Ot[tt * OS + 8 * rc]);
                         if (tb + tt < n)
-                            *reinterpret_cast<u32x4 *>(reinterpret_cast<TOut *>(a.out) +
-                                (((long)b * n + tb + tt) * a.Hq + (long)G * group + h) * D + 8 * rc) = w;
+                            st_stream(reinterpret_cast<TOut *>(a.out) +
+                                          (((long)b * n + tb + tt) * a.Hq + (long)G * group + h) * D + 8 * rc, w);
                     }
                     __builtin_amdgcn_wave_barrier();
                 }

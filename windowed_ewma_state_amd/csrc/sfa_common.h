@@ -78,6 +78,14 @@ __device__ __forceinline__ void store2(__bf16 *p, float a, float b) {
     *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(a, b);
 }
 
+// streaming (non-temporal) 16-byte accesses for data touched exactly once
+__device__ __forceinline__ u32x4 ld_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void st_stream(void *p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
 // MFMA wrappers
 __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

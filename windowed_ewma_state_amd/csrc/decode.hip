@@ -18,6 +18,7 @@
 //   PV       VALU fp32, lane l owns head-dim elements [l*d/64, (l+1)*d/64),
 //            probabilities broadcast through LDS.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "sfa_common.h"
@@ -26,6 +27,8 @@
 namespace sfa {
 
 namespace {
+
+constexpr int kMaxDevices = 64;
 
 constexpr int kUnitsPerBlock = 4;
 
@@ -196,8 +199,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 // k_decode_mfma: bf16 inputs, up to 16 query heads per KV head.
 //
 // Each wave walks units (layer, sequence, KV head) with a stride of the grid's
-// wave count and prefetches the next unit's loads while it computes the
-// current one.  Per unit:
+// wave count and prefetches the next unit's loads into the second of two
+// register buffers while it computes the current one.  Slots past the valid
+// ones and heads past the group read a valid row instead of being zero-filled:
+// their probabilities are exactly 0 and their outputs are never stored.  Per unit:
 //   scores  one v_mfma_f32_16x16x32_bf16 tile per 32 head-dim elements:
 //           A = ring K rows (row = slot, the new key in slot pos mod W),
 //           B = queries (column = head); lane holds P[head l%16][slots 4(l/16)+i]
@@ -230,186 +235,224 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     const int lb = unit / a.Hkv;
     const int b = lb % a.B;
     const int W = a.W, group = a.group;
-    const int p = a.pos[b];
+    const int p = __builtin_amdgcn_readfirstlane(a.pos[b]);
     u.p = p;
-    const int s = p >= 0 ? p % W : 0;
+    if (p < 0) return;  // skipped unit (uniform)
+    const int s = p % W;
     const int nvalid = (p >= W - 1) ? W : p + 1;
     const __bf16 *ringK = reinterpret_cast<const __bf16 *>(a.ring_k) + (long)unit * W * D;
     const __bf16 *ringV = reinterpret_cast<const __bf16 *>(a.ring_v) + (long)unit * W * D;
     const __bf16 *kn = reinterpret_cast<const __bf16 *>(a.k_new) + (long)unit * D;
     const __bf16 *vn = reinterpret_cast<const __bf16 *>(a.v_new) + (long)unit * D;
     const __bf16 *qg = reinterpret_cast<const __bf16 *>(a.q) + ((long)lb * a.Hq + G * group) * D;
-    const bool live = p >= 0;
     // score operands: A = ring K row of slot c16 (the new key in slot pos mod W),
-    // B = query of head c16; 8 head-dim elements per lane
-    const __bf16 *krow = (c16 == s) ? kn : ringK + (long)c16 * D;
+    // B = query of head c16; 8 head-dim elements per lane.  Rows past the valid
+    // slots / heads are clamped to a valid row: their scores are masked and
+    // their outputs never stored, so no zero fill is needed.
+    const int krow_i = c16 < nvalid ? c16 : s;
+    const __bf16 *krow = (krow_i == s) ? kn : ringK + (long)krow_i * D;
+    const __bf16 *qrow = qg + (long)(c16 < group ? c16 : group - 1) * D;
 #pragma unroll
     for (int st = 0; st < D / 32; ++st) {
-        u.kop[st] = bf16x8{};
-        u.qop[st] = bf16x8{};
-        if (live && c16 < W) u.kop[st] = __builtin_bit_cast(bf16x8, ld_stream(krow + 32 * st + 8 * q4));
-        if (live && c16 < group) u.qop[st] = __builtin_bit_cast(bf16x8, ld_stream(qg + (long)c16 * D + 32 * st + 8 * q4));
+        u.kop[st] = __builtin_bit_cast(bf16x8, ld_stream(krow + 32 * st + 8 * q4));
+        u.qop[st] = __builtin_bit_cast(bf16x8, ld_stream(qrow + 32 * st + 8 * q4));
     }
     // V rows for the transpose: lane (m = lane % 8, c = lane / 8) holds slot rows
-    // 2m and 2m+1 at 16-byte chunks c (+ 8 for d 128)
+    // 2m and 2m+1 at 16-byte chunks c (+ 8 for d 128); invalid slots read the new
+    // value (finite data; their probability is exactly 0)
     const int m = lane & 7, c = lane >> 3;
 #pragma unroll
     for (int i = 0; i < UnitLoads<D>::VR; ++i) {
         const int r = 2 * m + (i & 1);
         const int ch = c + 8 * (i >> 1);
-        u.v[i] = u32x4{0u, 0u, 0u, 0u};
-        if (live && r < nvalid) {
-            const __bf16 *src = (r == s) ? vn : ringV + (long)r * D;
-            u.v[i] = ld_stream(src + 8 * ch);
-        }
+        const __bf16 *src = (r == s || r >= nvalid) ? vn : ringV + (long)r * D;
+        u.v[i] = ld_stream(src + 8 * ch);
     }
     // far-field state, evicted key, new key/value (e-pair layout)
     const int e0 = lane * EPL;
     const float *S_ptr = a.state + (long)unit * D + e0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) u.S[e] = live ? S_ptr[e] : 0.f;
+    for (int e = 0; e < EPL; ++e) u.S[e] = S_ptr[e];
+    const __bf16 *kev = ringK + (long)s * D + e0;  // position p-W when p >= W
     if (EPL == 2) {
-        const uint32_t kw = live && p >= W ? *reinterpret_cast<const uint32_t *>(ringK + (long)s * D + e0) : 0u;
+        const uint32_t kw = *reinterpret_cast<const uint32_t *>(kev);
         u.kev[0] = bf16_lo(kw);
         u.kev[EPL - 1] = bf16_hi(kw);
-        u.kn = live ? *reinterpret_cast<const uint32_t *>(kn + e0) : 0u;
-        u.vn = live ? *reinterpret_cast<const uint32_t *>(vn + e0) : 0u;
+        u.kn = *reinterpret_cast<const uint32_t *>(kn + e0);
+        u.vn = *reinterpret_cast<const uint32_t *>(vn + e0);
     } else {
-        const uint32_t kw = live && p >= W ? *reinterpret_cast<const uint16_t *>(ringK + (long)s * D + e0) : 0u;
+        const uint32_t kw = *reinterpret_cast<const uint16_t *>(kev);
         u.kev[0] = bf16_bits_to_f32(kw);
-        u.kn = live ? *reinterpret_cast<const uint16_t *>(kn + e0) : 0u;
-        u.vn = live ? *reinterpret_cast<const uint16_t *>(vn + e0) : 0u;
+        u.kn = *reinterpret_cast<const uint16_t *>(kn + e0);
+        u.vn = *reinterpret_cast<const uint16_t *>(vn + e0);
+    }
+}
+
+template <typename TOut, int D>
+__device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, const UnitLoads<D> &u, int lane,
+                                             __bf16 *vt, float *sl) {
+    constexpr int EPL = D / kWave;
+    constexpr int VTS = kMaxWindow + 4;
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const int W = a.W, group = a.group;
+    const int e0 = lane * EPL;
+    const int p = u.p;
+    if (p >= 0) {
+        const int G = unit % a.Hkv;
+        const int lb = unit / a.Hkv;
+        const int l = lb / a.B;
+        const int s = p % W;
+        const int nvalid = (p >= W - 1) ? W : p + 1;
+        // far field: the key of position p-W leaves the window
+        const float gm = a.gamma[(long)l * a.Hkv + G];
+        float S[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * u.kev[e] : u.S[e];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sl[e0 + e] = S[e];
+        // V^T tile: row = head-dim element, 16 slots per row; consecutive
+        // lanes write consecutive dwords (slot pairs)
+        const int m = lane & 7, c = lane >> 3;
+#pragma unroll
+        for (int pr = 0; pr < UnitLoads<D>::VR / 2; ++pr) {
+            const int ch = c + 8 * pr;
+            const u32x4 va = u.v[2 * pr], vb = u.v[2 * pr + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
+                const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
+                *reinterpret_cast<uint32_t *>(&vt[(8 * ch + 2 * i) * VTS + 2 * m]) = lo;
+                *reinterpret_cast<uint32_t *>(&vt[(8 * ch + 2 * i + 1) * VTS + 2 * m]) = hi;
+            }
+        }
+        // scores and softmax over the valid slots
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) sc = mfma_bf16_16x16x32(u.kop[st], u.qop[st], sc);
+        float x[4], mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = (4 * q4 + i < nvalid) ? sc[i] * a.scale_log2e : -INFINITY;
+            mx = fmaxf(mx, x[i]);
+        }
+        mx = max_over_groups(mx);
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = (4 * q4 + i < nvalid) ? __builtin_amdgcn_exp2f(x[i] - mx) : 0.f;
+            sum += x[i];
+        }
+        const float inv = 1.f / sum_over_groups(sum);
+        bf16x4_t Ph, Pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __bf16 h, lo_;
+            split_bf16(x[i] * inv, h, lo_);
+            Ph[i] = h;
+            Pl[i] = lo_;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        const bool head_ok = c16 < group;
+        const float al = head_ok ? a.alpha[(long)l * a.Hq + (long)G * group + c16] : 0.f;
+        TOut *orow = reinterpret_cast<TOut *>(a.out) + ((long)lb * a.Hq + G * group + c16) * D;
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+            float ov[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int drow = 32 * k + 8 * (c16 >> 2) + 4 * half + (c16 & 3);
+                const bf16x4_t vop = __builtin_bit_cast(bf16x4_t, *reinterpret_cast<const u32x2 *>(&vt[drow * VTS + 4 * q4]));
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, Ph, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, Pl, o, 0, 0, 0);
+                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sl[32 * k + 8 * q4 + 4 * half]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[4 * half + i] = fmaf(al, s4[i], o[i]);
+            }
+            if (head_ok) {
+                if constexpr (std::is_same<TOut, float>::value) {
+                    *reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+                    *reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4 + 4) = make_float4(ov[4], ov[5], ov[6], ov[7]);
+                } else {
+                    u32x4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
+                    st_stream(orow + 32 * k + 8 * q4, w);
+                }
+            }
+        }
+        // cache update (every read of this unit's ring is done)
+        float *S_ptr = a.state + (long)unit * D + e0;
+        __bf16 *ringK = reinterpret_cast<__bf16 *>(a.ring_k) + ((long)unit * W + s) * D + e0;
+        __bf16 *ringV = reinterpret_cast<__bf16 *>(a.ring_v) + ((long)unit * W + s) * D + e0;
+        if constexpr (EPL == 2) {
+            *reinterpret_cast<float2 *>(S_ptr) = make_float2(S[0], S[EPL - 1]);
+            *reinterpret_cast<uint32_t *>(ringK) = u.kn;
+            *reinterpret_cast<uint32_t *>(ringV) = u.vn;
+        } else {
+            S_ptr[0] = S[0];
+            *reinterpret_cast<uint16_t *>(ringK) = (uint16_t)u.kn;
+            *reinterpret_cast<uint16_t *>(ringV) = (uint16_t)u.vn;
+        }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
 template <typename TOut, int D>
 __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
-    constexpr int EPL = D / kWave;
     constexpr int VTS = kMaxWindow + 4;  // V^T row stride (bf16): 16 slots + pad
     __shared__ __attribute__((aligned(16))) __bf16 Vt[4][D * VTS];
     __shared__ __attribute__((aligned(16))) float Sl[4][D];
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int q4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int n_units = a.L * a.B * a.Hkv;
     const int stride = gridDim.x * 4;
     int unit = blockIdx.x * 4 + wave;
-    const int W = a.W, group = a.group;
-    const int e0 = lane * EPL;
     __bf16 *vt = Vt[wave];
     float *sl = Sl[wave];
 
-    UnitLoads<D> cur;
-    if (unit < n_units) unit_load<D>(a, unit, cur, lane);
-    for (; unit < n_units; unit += stride) {
-        UnitLoads<D> nxt;  // the next unit's loads are in flight while this one computes
-        if (unit + stride < n_units) unit_load<D>(a, unit + stride, nxt, lane);
-
-        const int p = cur.p;
-        if (p >= 0) {
-            const int G = unit % a.Hkv;
-            const int lb = unit / a.Hkv;
-            const int l = lb / a.B;
-            const int s = p % W;
-            const int nvalid = (p >= W - 1) ? W : p + 1;
-            // far field: the key of position p-W leaves the window
-            const float gm = a.gamma[(long)l * a.Hkv + G];
-            float S[EPL];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * cur.S[e] + (1.f - gm) * cur.kev[e] : cur.S[e];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) sl[e0 + e] = S[e];
-            // V^T tile: row = head-dim element, 16 slots per row; consecutive
-            // lanes write consecutive dwords (slot pairs)
-            const int m = lane & 7, c = lane >> 3;
-#pragma unroll
-            for (int pr = 0; pr < UnitLoads<D>::VR / 2; ++pr) {
-                const int ch = c + 8 * pr;
-                const u32x4 va = cur.v[2 * pr], vb = cur.v[2 * pr + 1];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
-                    const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
-                    *reinterpret_cast<uint32_t *>(&vt[(8 * ch + 2 * i) * VTS + 2 * m]) = lo;
-                    *reinterpret_cast<uint32_t *>(&vt[(8 * ch + 2 * i + 1) * VTS + 2 * m]) = hi;
-                }
-            }
-            // scores and softmax over the valid slots
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < D / 32; ++st) sc = mfma_bf16_16x16x32(cur.kop[st], cur.qop[st], sc);
-            float x[4], mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = (4 * q4 + i < nvalid) ? sc[i] * a.scale_log2e : -INFINITY;
-                mx = fmaxf(mx, x[i]);
-            }
-            mx = max_over_groups(mx);
-            float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = (4 * q4 + i < nvalid) ? __builtin_amdgcn_exp2f(x[i] - mx) : 0.f;
-                sum += x[i];
-            }
-            const float inv = 1.f / sum_over_groups(sum);
-            bf16x4_t Ph, Pl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __bf16 h, lo_;
-                split_bf16(x[i] * inv, h, lo_);
-                Ph[i] = h;
-                Pl[i] = lo_;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-            const bool head_ok = c16 < group;
-            const float al = head_ok ? a.alpha[(long)l * a.Hq + (long)G * group + c16] : 0.f;
-            TOut *orow = reinterpret_cast<TOut *>(a.out) + ((long)lb * a.Hq + G * group + c16) * D;
-#pragma unroll
-            for (int k = 0; k < D / 32; ++k) {
-                float ov[8];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int drow = 32 * k + 8 * (c16 >> 2) + 4 * half + (c16 & 3);
-                    const bf16x4_t vop = __builtin_bit_cast(bf16x4_t, *reinterpret_cast<const u32x2 *>(&vt[drow * VTS + 4 * q4]));
-                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, Ph, o, 0, 0, 0);
-                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, Pl, o, 0, 0, 0);
-                    const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sl[32 * k + 8 * q4 + 4 * half]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ov[4 * half + i] = fmaf(al, s4[i], o[i]);
-                }
-                if (head_ok) {
-                    if constexpr (std::is_same<TOut, float>::value) {
-                        *reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-                        *reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4 + 4) = make_float4(ov[4], ov[5], ov[6], ov[7]);
-                    } else {
-                        u32x4 w;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
-                        st_stream(orow + 32 * k + 8 * q4, w);
-                    }
-                }
-            }
-            // cache update (every read of this unit's ring is done)
-            float *S_ptr = a.state + (long)unit * D + e0;
-            __bf16 *ringK = reinterpret_cast<__bf16 *>(a.ring_k) + ((long)unit * W + s) * D + e0;
-            __bf16 *ringV = reinterpret_cast<__bf16 *>(a.ring_v) + ((long)unit * W + s) * D + e0;
-            if constexpr (EPL == 2) {
-                *reinterpret_cast<float2 *>(S_ptr) = make_float2(S[0], S[EPL - 1]);
-                *reinterpret_cast<uint32_t *>(ringK) = cur.kn;
-                *reinterpret_cast<uint32_t *>(ringV) = cur.vn;
-            } else {
-                S_ptr[0] = S[0];
-                *reinterpret_cast<uint16_t *>(ringK) = (uint16_t)cur.kn;
-                *reinterpret_cast<uint16_t *>(ringV) = (uint16_t)cur.vn;
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
-        cur = nxt;
+    // two register buffers in turn: the next unit's loads are in flight while
+    // the current one computes
+    UnitLoads<D> A, Bf;
+    if (unit < n_units) unit_load<D>(a, unit, A, lane);
+    while (unit < n_units) {
+        if (unit + stride < n_units) unit_load<D>(a, unit + stride, Bf, lane);
+        unit_compute<TOut, D>(a, unit, A, lane, vt, sl);
+        unit += stride;
+        if (unit >= n_units) break;
+        if (unit + stride < n_units) unit_load<D>(a, unit + stride, A, lane);
+        unit_compute<TOut, D>(a, unit, Bf, lane, vt, sl);
+        unit += stride;
     }
+}
+
+// Grid of one wave per (unit, unit + stride, ...) chain: no more blocks than the
+// device holds at once (one round of waves, no partly filled tail round), and
+// at least two units per wave so that every wave overlaps a prefetch with compute.
+template <typename K>
+hipError_t launch_persistent(K kernel, const DecodeArgs &a, long units, hipStream_t stream) {
+    static std::atomic<int> resident[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int cap = resident[dev].load(std::memory_order_relaxed);
+    if (cap == 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+        if (e != hipSuccess) return e;
+        cap = std::max(1, cus * std::max(1, per_cu));
+        resident[dev].store(cap, std::memory_order_relaxed);
+    }
+    const long blocks = std::max<long>(1, std::min<long>(cap, (units + 7) / 8));
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 template <typename TIn, typename TOut>
@@ -417,13 +460,8 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
     const long units = (long)a.L * a.B * a.Hkv;
     if constexpr (std::is_same<TIn, __bf16>::value) {
         if (a.group <= 16) {
-            // about four units per wave, so each wave overlaps a prefetch with compute
-            const long blocks = std::min<long>((units + 15) / 16, 65535);
-            if (a.d == 128)
-                hipLaunchKernelGGL((k_decode_mfma<TOut, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-            else
-                hipLaunchKernelGGL((k_decode_mfma<TOut, 64>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-            return hipGetLastError();
+            if (a.d == 128) return launch_persistent(k_decode_mfma<TOut, 128>, a, units, stream);
+            return launch_persistent(k_decode_mfma<TOut, 64>, a, units, stream);
         }
     }
     const dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock));

@@ -53,7 +53,7 @@ __device__ __forceinline__ void load_epl(const T *p, float *x) {
 
 // ---------------------------------------------------------------------------
 // k_ewma_agg: local aggregates A (EWMA from zero) of 16-token blocks and tiles.
-// One wave per 64-token tile (four tiles per workgroup).  Lane (w, c) owns the
+// One wave per 64-token tile of one (b, KV head) chain (four chains per workgroup).  Lane (w, c) owns the
 // 16-byte chunk c of the head dimension for block w of the tile, so every load
 // is a 16-byte vector and a block's 16 rows are in flight together.
 // ---------------------------------------------------------------------------
@@ -65,9 +65,12 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     constexpr int CPL = CPR / LPB > 0 ? CPR / LPB : 1;  // chunks per lane
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tiles_per_bg = a.ntiles;
-    const int gt = blockIdx.x * 4 + wave;  // global tile index over (bg, tile)
-    if (gt >= a.B * a.Hkv * tiles_per_bg) return;
-    const int tile = gt % tiles_per_bg, bg = gt / tiles_per_bg;
+    // chain fastest: the waves of a workgroup take the same tile of consecutive
+    // (b, KV head) chains, i.e. neighbouring 256-byte pieces of the same rows
+    const int nbg = a.B * a.Hkv;
+    const int gt = blockIdx.x * 4 + wave;
+    if (gt >= nbg * tiles_per_bg) return;
+    const int tile = gt / nbg, bg = gt - tile * nbg;
     const int b = bg / a.Hkv, G = bg % a.Hkv;
     const int n = a.n, W = a.W;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
@@ -163,8 +166,8 @@ __device__ __forceinline__ int evict_steps(int p0, int s0, int len, int W) {
 // k_ewma_carry: S before each tile (exclusive scan over tiles) and final S.
 // One workgroup per (b, KV head, 16 head-dim elements); 64 parts of the tile
 // range are scanned in parallel (all loads of a part issued together), the
-// part aggregates are combined through LDS, and each part is rescanned from
-// its carry-in.
+// part aggregates are combined by a log-step scan through LDS, and each part
+// is rescanned from its carry-in.
 // ---------------------------------------------------------------------------
 constexpr int kCarryParts = 64, kCarryCols = 16;
 
@@ -198,11 +201,26 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
         X = gl * X + A[(long)i * D];
         Gam *= gl;
     }
-    partX[part][threadIdx.x % kCarryCols] = X;
-    if (threadIdx.x % kCarryCols == 0) partG[part] = Gam;
+    // inclusive scan of the part aggregates (X, Γ) over parts, log2(parts) steps:
+    // (X_a, Γ_a) then (X_b, Γ_b) combine to (Γ_b·X_a + X_b, Γ_a·Γ_b)
+    const int col = threadIdx.x % kCarryCols;
+#pragma unroll
+    for (int off = 1; off < kCarryParts; off <<= 1) {
+        partX[part][col] = X;
+        if (col == 0) partG[part] = Gam;
+        __syncthreads();
+        if (part >= off) {
+            X = Gam * partX[part - off][col] + X;
+            Gam = partG[part - off] * Gam;
+        }
+        __syncthreads();
+    }
+    partX[part][col] = X;
+    if (col == 0) partG[part] = Gam;
     __syncthreads();
+    // carry into this part: S_init through all earlier parts
     float C = S_init;
-    for (int q = 0; q < part; ++q) C = partG[q] * C + partX[q][threadIdx.x % kCarryCols];
+    if (part > 0) C = partG[part - 1] * S_init + partX[part - 1][col];
     float *Cout = a.carry + (long)bg * nt * D + e;
     X = C;
 #pragma unroll 8

@@ -267,8 +267,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: every kernel here runs on a single MI355X "
-              "(see the sharding notes in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: every kernel here runs on a single MI355X and "
+              "there is no multi-GPU path to time; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

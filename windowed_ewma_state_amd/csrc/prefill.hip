@@ -235,8 +235,14 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
 // k_window_attn: windowed softmax attention + α·S epilogue
 // ---------------------------------------------------------------------------
 template <typename TIn> struct Lds;
-template <> struct Lds<__bf16> { static constexpr int kpad = 8, vpad = 8; };
+template <> struct Lds<__bf16> { static constexpr int kpad = 8, vpad = 0; };
 template <> struct Lds<float> { static constexpr int kpad = 4, vpad = 4; };
+
+// bf16 V^T tile: rows of 80 keys (40 dwords) with the dword column XORed by
+// 2·((row / 8) mod 4).  The PV operand reads of 16 lanes hit rows r + 8a + b
+// (a, b < 4): the row stride alone maps a to the same banks, the XOR moves the
+// four a to distinct dword pairs, so a read is free of bank conflicts.
+__device__ __forceinline__ int vt_dword(int row, int col) { return row * (kRows / 2) + (col ^ (2 * ((row >> 3) & 3))); }
 
 template <typename TOut>
 __device__ __forceinline__ void store4(TOut *p, f32x4 v);
@@ -361,8 +367,8 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
                 const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
-                *reinterpret_cast<uint32_t *>(&Vt[(c * EPC + 2 * i) * VS + 2 * m]) = lo;
-                *reinterpret_cast<uint32_t *>(&Vt[(c * EPC + 2 * i + 1) * VS + 2 * m]) = hi;
+                reinterpret_cast<uint32_t *>(Vt)[vt_dword(c * EPC + 2 * i, m)] = lo;
+                reinterpret_cast<uint32_t *>(Vt)[vt_dword(c * EPC + 2 * i + 1, m)] = hi;
             }
             if (write_ring) {
                 if (ta >= t0 && ta < n && ta >= n - W)
@@ -444,7 +450,8 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             for (int st = 0; st < D / 32; ++st)
                 Kc[T][st] = *reinterpret_cast<const bf16x8 *>(
                     &Klds[(kBlk * wave + 16 * T + c16) * KS + 32 * st + 8 * q4]);
-        const TIn *vrow0 = &Vt[kBlk * wave + 4 * q4];   // + d * VS: keys 4q4.. of T0, +16: of T1
+        const uint32_t *vt32 = reinterpret_cast<const uint32_t *>(Vt);
+        const int vcol = (kBlk * wave + 4 * q4) / 2;   // dword column of keys 4q4.. of T0 (+8: of T1)
         const float *Srow = &Sw[c16 * SS + 8 * q4];     // S of token c16 at d = 32k + 8q4 + e
         // bf16 outputs go through a per-wave [16 tokens][D] tile in the K staging
         // area (free once every wave holds its K operands) so that each store
@@ -519,9 +526,9 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const int drow = 32 * k + 8 * (c16 >> 2) + 4 * half + (c16 & 3);
-                        const TIn *vr = vrow0 + drow * VS;
+                        const uint32_t *vr = vt32 + vt_dword(drow, vcol);
                         const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
-                        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
+                        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 8);
                         const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                         f32x4 o = {0.f, 0.f, 0.f, 0.f};
                         o = mfma_bf16_16x16x32(vop, Ph, o);

@@ -201,11 +201,12 @@ __global__ __launch_bounds__(256) void k_field_carry(EnhanceArgs a) {
 // ---------------------------------------------------------------------------
 // k_enhance
 // ---------------------------------------------------------------------------
+// eight attention values (raw 16-byte words) -> bf16 hi (+ lo for fp32) and Σa²
 template <typename TIn>
-__device__ __forceinline__ void load_a8(const TIn *p, bf16x8 &hi, bf16x8 &lo, float &sq);
+__device__ __forceinline__ void split_a8(const u32x4 *w, bf16x8 &hi, bf16x8 &lo, float &sq);
 template <>
-__device__ __forceinline__ void load_a8<__bf16>(const __bf16 *p, bf16x8 &hi, bf16x8 &lo, float &sq) {
-    hi = *reinterpret_cast<const bf16x8 *>(p);
+__device__ __forceinline__ void split_a8<__bf16>(const u32x4 *w, bf16x8 &hi, bf16x8 &lo, float &sq) {
+    hi = __builtin_bit_cast(bf16x8, w[0]);
     lo = bf16x8{};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -214,17 +215,15 @@ __device__ __forceinline__ void load_a8<__bf16>(const __bf16 *p, bf16x8 &hi, bf1
     }
 }
 template <>
-__device__ __forceinline__ void load_a8<float>(const float *p, bf16x8 &hi, bf16x8 &lo, float &sq) {
-    const float4 v0 = *reinterpret_cast<const float4 *>(p);
-    const float4 v1 = *reinterpret_cast<const float4 *>(p + 4);
-    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+__device__ __forceinline__ void split_a8<float>(const u32x4 *w, bf16x8 &hi, bf16x8 &lo, float &sq) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+        const float v = __uint_as_float(w[e >> 2][e & 3]);
         __bf16 h, l;
-        split_bf16(v[e], h, l);
+        split_bf16(v, h, l);
         hi[e] = h;
         lo[e] = l;
-        sq = fmaf(v[e], v[e], sq);
+        sq = fmaf(v, v, sq);
     }
 }
 
@@ -259,20 +258,26 @@ template <typename TIn, typename TOut>
 __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
     constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split a as well
     constexpr int XS = kCols + 4;                                // LDS row stride (floats)
-    // phase 1 exchange (cosine partials) aliases the phase 2 buffers (scan output)
+    // phase 4 stages a quarter of the tile's columns (256) for tokens tb-16 ..
+    // tb+63 in LDS, aliasing the phase 1 exchange (cosine partials)
+    constexpr int kRowsE = kBlk + kTile;          // staged rows: tokens tb-16 .. tb+63
+    constexpr int kQCols = 4 * kCols;             // columns per quarter, one 64-column chunk per wave
+    constexpr int EPC = 16 / sizeof(TIn);         // elements per 16-byte piece
+    constexpr int QCH = kQCols / EPC;             // 16-byte pieces per staged row
+    constexpr int AS = kQCols + EPC;              // staged row stride (elements)
+    constexpr int NST = kRowsE * QCH / 256;       // staging loads per thread
+    static_assert(kRowsE * QCH % 256 == 0, "staging must split evenly over the workgroup");
     struct Phase1 {
         f32x4 cp[4][2][4][64];  // [wave][slot tile in round][token group][lane]
         float sq[4][4][64];     // [wave][token group][lane]
     };
-    struct Phase2 {
-        float X[4][kBlk * XS];  // per wave: ring mean/R + 0.5·field for 16 tokens x 64 columns
-        float A[4][kBlk * XS];  // per wave: the attention values of the same block
-    };
-    __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(Phase1) > sizeof(Phase2)
-                                                               ? sizeof(Phase1) : sizeof(Phase2)];
+    constexpr int kStageBytes = kRowsE * AS * (int)sizeof(TIn);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(Phase1) > kStageBytes
+                                                               ? sizeof(Phase1) : kStageBytes];
+    __shared__ __attribute__((aligned(16))) float Xs[4][kBlk * XS];  // per wave: ring mean/R + 0.5·field
     __shared__ __attribute__((aligned(16))) u32x4 Wx[4][2][2][64];  // [tg][ks][hi/lo][lane]
     Phase1 &p1 = *reinterpret_cast<Phase1 *>(smem);
-    Phase2 &p2 = *reinterpret_cast<Phase2 *>(smem);
+    TIn *Ast = reinterpret_cast<TIn *>(smem);
 
     const int lid = xcd_remap(blockIdx.x, a.L * a.ntiles);
     const int l = lid / a.ntiles, tile = lid % a.ntiles;
@@ -308,27 +313,82 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
         tok_ok[tg] = t < T;
         arow[tg] = Ag + (long)(tok_ok[tg] ? t : tb) * H + 8 * q4;
     }
-    for (int ks = ks0; ks < ks1; ++ks) {
+    // k-step operands: attention values of the four token groups and the pool
+    // tiles; two buffers in turn, so one k-step's loads fly while the other
+    // k-step's MFMAs run
+    constexpr int AW = kPrecise ? 2 : 1;  // 16-byte loads per token group
+    struct Ops {
+        u32x4 a[4][AW];
+        bf16x8 ph[4], pl[4];
+    };
+    auto load_ops = [&](int ks, Ops &o) {
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+            for (int h = 0; h < AW; ++h)
+                o.a[tg][h] = *reinterpret_cast<const u32x4 *>(arow[tg] + 32 * ks + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < nj) {
+                const uint16_t *op = poolA + (((long)ks * 4 + j) * 2) * kOpElems;
+                o.ph[j] = get8(op);
+                o.pl[j] = get8(op + kOpElems);
+            }
+        }
+    };
+    auto compute_ops = [&](const Ops &o) {
         bf16x8 bh[4], bl[4];
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-            load_a8<TIn>(arow[tg] + 32 * ks, bh[tg], bl[tg], sq[tg]);
+            split_a8<TIn>(o.a[tg], bh[tg], bl[tg], sq[tg]);
             if (!tok_ok[tg]) bh[tg] = bl[tg] = bf16x8{};
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j < nj) {
-                const uint16_t *op = poolA + (((long)ks * 4 + j) * 2) * kOpElems;
-                const bf16x8 ph = get8(op), plo = get8(op + kOpElems);
 #pragma unroll
                 for (int tg = 0; tg < 4; ++tg) {
-                    C[j][tg] = mfma_bf16_16x16x32(ph, bh[tg], C[j][tg]);
-                    C[j][tg] = mfma_bf16_16x16x32(plo, bh[tg], C[j][tg]);
-                    if constexpr (kPrecise) C[j][tg] = mfma_bf16_16x16x32(ph, bl[tg], C[j][tg]);
+                    C[j][tg] = mfma_bf16_16x16x32(o.ph[j], bh[tg], C[j][tg]);
+                    C[j][tg] = mfma_bf16_16x16x32(o.pl[j], bh[tg], C[j][tg]);
+                    if constexpr (kPrecise) C[j][tg] = mfma_bf16_16x16x32(o.ph[j], bl[tg], C[j][tg]);
                 }
             }
         }
+    };
+    {
+        Ops o0, o1;
+        if (ks0 < ks1) load_ops(ks0, o0);
+        for (int ks = ks0; ks < ks1; ks += 2) {
+            if (ks + 1 < ks1) load_ops(ks + 1, o1);
+            compute_ops(o0);
+            if (ks + 1 >= ks1) break;
+            if (ks + 2 < ks1) load_ops(ks + 2, o0);
+            compute_ops(o1);
+        }
     }
+    // the first column quarter's staging loads fly during phases 2 and 3
+    u32x4 stg[NST];
+    auto stage_load = [&](int q) {
+#pragma unroll
+        for (int k = 0; k < NST; ++k) {
+            const int idx = threadIdx.x + 256 * k;
+            const int r = idx / QCH, c = idx % QCH;
+            const int t = tb - kBlk + r;
+            const int col = q * kQCols + c * EPC;
+            stg[k] = u32x4{0u, 0u, 0u, 0u};
+            if (t >= 0 && t < T && col < H) stg[k] = *reinterpret_cast<const u32x4 *>(Ag + (long)t * H + col);
+        }
+    };
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int k = 0; k < NST; ++k) {
+            const int idx = threadIdx.x + 256 * k;
+            const int r = idx / QCH, c = idx % QCH;
+            *reinterpret_cast<u32x4 *>(&Ast[r * AS + c * EPC]) = stg[k];
+        }
+    };
+    stage_load(0);
+
     // ---- (2) reduce the four partials: wave w ends with token group tg = w -------
     f32x4 Cw[4];
 #pragma unroll
@@ -393,7 +453,9 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
     }
     __syncthreads();
 
-    // ---- (4) this wave's column chunks: scan, semantic sum, epilogue --------------
+    // ---- (4) column quarters: stage, then each wave scans its 64-column chunk ----
+    // from LDS (ring mean and field along the tokens), and per 16-token group
+    // does the semantic sum (MFMA) and the epilogue
     const float g = a.ema_gamma;
     const float invR = 1.f / (float)R;
     const int len = min(kTile, T - tb);
@@ -401,71 +463,65 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
     const int ring0 = a.t0 % R;   // slot of relative token 0
     const bool reach_ring = tb < R;  // only the first tile looks back before token 0
     const float *carry = a.carry + ((long)l * a.ntiles + tile) * H;
-    float *Xw = p2.X[wave];
-    float *Aw = p2.A[wave];
+    float *Xw = Xs[wave];
     TOut *Og = reinterpret_cast<TOut *>(a.out) + (long)l * T * H;
     float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
     const int nch = H / kCols;
-    const int ch0 = wave * nch / 4, ch1 = (wave + 1) * nch / 4;
+    const int nq = (H + kQCols - 1) / kQCols;
 
-    for (int ch = ch0; ch < ch1; ++ch) {
+    for (int q = 0; q < nq; ++q) {
+        __syncthreads();  // the previous quarter (or phase 1) is done with the LDS
+        stage_store();
+        if (q + 1 < nq) stage_load(q + 1);
+        __syncthreads();
+        const int ch = 4 * q + wave;
+        if (ch >= nch) continue;  // wave-uniform: a partial last quarter
         const int xc = ch * kCols;
         const int x = xc + lane;
+        const int xq = wave * kCols;  // the chunk's first column within the quarter
         // the chunk's semantic-sum A operands (4 column tiles x k-steps x hi/lo),
-        // shared by its four token groups; issued before the scan's loads
+        // shared by its four token groups
         bf16x8 pt[kCols / 16][4];
 #pragma unroll
         for (int xt = 0; xt < kCols / 16; ++xt)
 #pragma unroll
             for (int o = 0; o < 4; ++o) pt[xt][o] = get8(poolT + ((long)(xc / 16 + xt) * 4 + o) * kOpElems);
-        // value of relative token t at column x; -R <= t < 0 reads the carried
-        // ring, slot (t0 + t) mod R = ring0 + t (+R when negative)
-        const TIn *Acol = Ag + x;
+        // value of relative token t (-16 <= t < 64) at column x: staged, or for
+        // t < 0 in the first tile the carried ring, slot (t0 + t) mod R
         auto val = [&](int t) -> float {
             if (reach_ring && t < 0) {
                 const int slot = ring0 + t < 0 ? ring0 + t + R : ring0 + t;
                 return ringl[(long)slot * H + x];
             }
-            return t < T ? Elem<TIn>::load(Acol + (long)t * H) : 0.f;
+            return (float)Ast[(kBlk + t) * AS + xq + lane];
         };
-        // ring sum of tokens tb-R .. tb-1, then slide: + token j, - token j-R
+        // ring sum of tokens -R .. -1, then slide: + token t, - token t-R
         float rs = 0.f;
-        {
-            float pre[kBlk];
 #pragma unroll
-            for (int k = 0; k < kBlk; ++k) pre[k] = (k < R) ? val(tb - 1 - k) : 0.f;
-#pragma unroll
-            for (int k = 0; k < kBlk; ++k) rs += pre[k];
-        }
+        for (int k = 0; k < kBlk; ++k)
+            if (k < R) rs += val(-1 - k);
         float F = carry[x];
         for (int tg = 0; tg < 4; ++tg) {
             const int j0 = 16 * tg;
             if (j0 >= len) break;  // wave-uniform
-            // this token group's softmax weights (B operands), from LDS
+#pragma unroll
+            for (int j = 0; j < kBlk; ++j) {
+                const int t = j0 + j;
+                if (t < len) {
+                    const float cur = val(t);
+                    rs += cur - val(t - R);
+                    F = g * F + (1.f - g) * cur;
+                }
+                Xw[j * XS + lane] = rs * invR + 0.5f * F;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const bf16x8 wh0 = __builtin_bit_cast(bf16x8, Wx[tg][0][0][lane]);
             const bf16x8 wl0 = __builtin_bit_cast(bf16x8, Wx[tg][0][1][lane]);
             const bf16x8 wh1 = __builtin_bit_cast(bf16x8, Wx[tg][1][0][lane]);
             const bf16x8 wl1 = __builtin_bit_cast(bf16x8, Wx[tg][1][1][lane]);
             const bool tok_ok_g = tb + j0 + c16 < T;
-            float cur[kBlk], old[kBlk];
-#pragma unroll
-            for (int j = 0; j < kBlk; ++j) {  // the block's loads are all in flight together
-                const bool ok = j0 + j < len;
-                cur[j] = ok ? val(tb + j0 + j) : 0.f;
-                old[j] = ok ? val(tb + j0 + j - R) : 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < kBlk; ++j) {
-                if (j0 + j < len) {
-                    rs += cur[j] - old[j];
-                    F = g * F + (1.f - g) * cur[j];
-                }
-                Xw[j * XS + lane] = rs * invR + 0.5f * F;
-                Aw[j * XS + lane] = cur[j];
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
             for (int xt = 0; xt < kCols / 16; ++xt) {
                 const bf16x8 th0 = pt[xt][0], tl0 = pt[xt][1], th1 = pt[xt][2], tl1 = pt[xt][3];
@@ -480,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
                 const int xl = 16 * xt + 4 * q4;
                 if (tok_ok_g) {
                     const f32x4 X4 = *reinterpret_cast<const f32x4 *>(&Xw[c16 * XS + xl]);
-                    const f32x4 A4 = *reinterpret_cast<const f32x4 *>(&Aw[c16 * XS + xl]);
+                    const f32x4 A4 = load4f<TIn>(&Ast[(kBlk + j0 + c16) * AS + xq + xl]);
                     f32x4 o, en;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {

@@ -534,20 +534,34 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
                 sm = mfma_bf16_16x16x32(tl1, wh1, sm);
                 // lane: sem[x = xc + 16xt + 4q4 + i][token tb + j0 + c16]
                 const int xl = 16 * xt + 4 * q4;
-                if (tok_ok_g) {
-                    const f32x4 X4 = *reinterpret_cast<const f32x4 *>(&Xw[c16 * XS + xl]);
-                    const f32x4 A4 = load4f<TIn>(&Ast[(kBlk + j0 + c16) * AS + xq + xl]);
-                    f32x4 o, en;
+                const f32x4 X4 = *reinterpret_cast<const f32x4 *>(&Xw[c16 * XS + xl]);
+                const f32x4 A4 = load4f<TIn>(&Ast[(kBlk + j0 + c16) * AS + xq + xl]);
+                f32x4 o, en;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = fminf(fmaxf(X4[i] + 0.5f * sm[i], -a.clip), a.clip);
-                        en[i] = al * e;
-                        o[i] = A4[i] + en[i];
-                    }
-                    const long off = (long)(tb + j0 + c16) * H + xc + xl;
-                    store4o<TOut>(Og + off, o);
-                    if (Eg) store4o<float>(Eg + off, en);
+                for (int i = 0; i < 4; ++i) {
+                    const float e = fminf(fmaxf(X4[i] + 0.5f * sm[i], -a.clip), a.clip);
+                    en[i] = al * e;
+                    o[i] = A4[i] + en[i];
                 }
+                // the output goes back into the X tile (row c16, same byte row): a
+                // bf16 value lands on fp32 columns [xl/2, xl/2 + 2), which every
+                // lane has read by this column tile, an fp32 value on its own spot
+                store4o<TOut>(reinterpret_cast<TOut *>(&Xw[c16 * XS]) + xl, o);
+                if (Eg && tok_ok_g) store4o<float>(Eg + (long)(tb + j0 + c16) * H + xc + xl, en);
+            }
+            // whole 128- or 256-byte rows of the 16 x 64 output tile
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            constexpr int OPR = kCols * (int)sizeof(TOut) / 16;  // 16-byte pieces per output row
+#pragma unroll
+            for (int k = 0; k < kBlk * OPR / 64; ++k) {
+                const int idx = lane + 64 * k;
+                const int r = idx / OPR, c = idx % OPR;
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(
+                    reinterpret_cast<const unsigned char *>(&Xw[r * XS]) + 16 * c);
+                if (j0 + r < len)
+                    st_stream(reinterpret_cast<unsigned char *>(Og + (long)(tb + j0 + r) * H + xc) + 16 * c, w);
             }
             __builtin_amdgcn_wave_barrier();
         }

@@ -230,6 +230,28 @@ def cpu_baseline(n_layers, budget_s=10.0):
                       f"(OpenMP over heads), wall time of the oracle call only"}
 
 
+def copy_ceiling(nbytes=1 << 30, reps=5):
+    """Device-to-device copy of 1 GiB (the runtime's copy kernel), timed with HIP
+    events: read + write bytes per second, the practical ceiling that a
+    streaming kernel with equal read and write traffic can be compared with."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = min(a.elapsed_time(b) for a, b in ev)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def copy_calibration(nbytes=1 << 30, reps=3):
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     dev = torch.device("cuda:0")
@@ -305,6 +327,7 @@ def main():
     if not args.no_secondary:
         res["decode"] = run_decode()
         res["enhance"] = run_enhance()
+        res["copy_ceiling_gbps"] = copy_ceiling()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.layers)
     print(json.dumps(res), flush=True)

@@ -472,46 +472,72 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
     for (int q = 0; q < nq; ++q) {
         __syncthreads();  // the previous quarter (or phase 1) is done with the LDS
         stage_store();
-        if (q + 1 < nq) stage_load(q + 1);
-        __syncthreads();
         const int ch = 4 * q + wave;
-        if (ch >= nch) continue;  // wave-uniform: a partial last quarter
+        const bool has = ch < nch;  // wave-uniform: a partial last quarter leaves waves idle
         const int xc = ch * kCols;
         const int x = xc + lane;
         const int xq = wave * kCols;  // the chunk's first column within the quarter
-        // the chunk's semantic-sum A operands (4 column tiles x k-steps x hi/lo),
-        // shared by its four token groups
+        // the chunk's own global reads go out before the next quarter's staging
+        // loads, so waiting for them never waits for the prefetch: the
+        // semantic-sum A operands (4 column tiles x k-steps x hi/lo, shared by
+        // the four token groups), the field carried into the tile, and in the
+        // first tile the R tokens before it from the carried ring, slot
+        // (t0 + t) mod R for t = -R..-1, parked in rows 16-R..15 of the X tile
         bf16x8 pt[kCols / 16][4];
+        float F = 0.f;
+        if (has) {
 #pragma unroll
-        for (int xt = 0; xt < kCols / 16; ++xt)
+            for (int xt = 0; xt < kCols / 16; ++xt)
 #pragma unroll
-            for (int o = 0; o < 4; ++o) pt[xt][o] = get8(poolT + ((long)(xc / 16 + xt) * 4 + o) * kOpElems);
-        // value of relative token t (-16 <= t < 64) at column x: staged, or for
-        // t < 0 in the first tile the carried ring, slot (t0 + t) mod R
-        auto val = [&](int t) -> float {
-            if (reach_ring && t < 0) {
-                const int slot = ring0 + t < 0 ? ring0 + t + R : ring0 + t;
-                return ringl[(long)slot * H + x];
+                for (int o = 0; o < 4; ++o) pt[xt][o] = get8(poolT + ((long)(xc / 16 + xt) * 4 + o) * kOpElems);
+            F = carry[x];
+            if (reach_ring) {
+#pragma unroll
+                for (int k = 0; k < kBlk; ++k) {
+                    const int t = k - kBlk;
+                    if (t >= -R) {
+                        const int slot = ring0 + t < 0 ? ring0 + t + R : ring0 + t;
+                        Xw[k * XS + lane] = ringl[(long)slot * H + x];
+                    }
+                }
             }
-            return (float)Ast[(kBlk + t) * AS + xq + lane];
+        }
+        if (q + 1 < nq) stage_load(q + 1);
+        __syncthreads();
+        if (!has) continue;
+        // value of relative token t (-16 <= t < 64) at column x: staged rows, or
+        // for t < 0 in the first tile the parked ring values
+        const TIn *Acol = Ast + xq + lane;
+        auto before = [&](int t) -> float {  // t < 0
+            const float xa = Xw[max(0, kBlk + t) * XS + lane];
+            const float sa = (float)Acol[(kBlk + t) * AS];
+            return reach_ring ? xa : sa;
         };
         // ring sum of tokens -R .. -1, then slide: + token t, - token t-R
         float rs = 0.f;
 #pragma unroll
-        for (int k = 0; k < kBlk; ++k)
-            if (k < R) rs += val(-1 - k);
-        float F = carry[x];
+        for (int k = 0; k < kBlk; ++k) {
+            const float v = before(-1 - k);
+            rs += k < R ? v : 0.f;
+        }
         for (int tg = 0; tg < 4; ++tg) {
             const int j0 = 16 * tg;
             if (j0 >= len) break;  // wave-uniform
+            // the group's 32 reads go out together; the first group takes the
+            // tokens before the tile where t - R < 0
+            float cur[kBlk], old[kBlk];
 #pragma unroll
             for (int j = 0; j < kBlk; ++j) {
                 const int t = j0 + j;
-                if (t < len) {
-                    const float cur = val(t);
-                    rs += cur - val(t - R);
-                    F = g * F + (1.f - g) * cur;
-                }
+                cur[j] = (float)Acol[(kBlk + t) * AS];
+                const float os = (float)Acol[(kBlk + t - R) * AS];
+                old[j] = (tg == 0 && t - R < 0) ? before(t - R) : os;
+            }
+#pragma unroll
+            for (int j = 0; j < kBlk; ++j) {
+                const bool ok = j0 + j < len;
+                rs = ok ? rs + (cur[j] - old[j]) : rs;
+                F = ok ? g * F + (1.f - g) * cur[j] : F;
                 Xw[j * XS + lane] = rs * invR + 0.5f * F;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

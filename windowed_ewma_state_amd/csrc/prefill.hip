@@ -340,6 +340,23 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             }
     }
 
+    // the S carried into the tile and the aggregates of this wave's earlier
+    // blocks (read in step 2) go out with the queries, ahead of the staging
+    const int e0 = lane * EPL;
+    float Cin[EPL], Ain[3][EPL];
+    {
+        const long tbase = (long)bg * a.ntiles + tile;
+        const float *C = a.carry + tbase * D + e0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) Cin[e] = C[e];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            const float *A = a.agg16 + (tbase * 4 + w) * D + e0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) Ain[w][e] = w < wave ? A[e] : 0.f;
+        }
+    }
+
     // ---- (1) stage K rows (row-major) and V (transposed) ---------------------
     for (int idx = tid; idx < kRows * CPR; idx += 256) {
         const int r = idx / CPR, c = idx % CPR;
@@ -394,19 +411,16 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     }
 
     // ---- (2) S just before this wave's 16-token block -----------------------
-    const int e0 = lane * EPL;
     float S[EPL];
-    {
-        const long tbase = (long)bg * a.ntiles + tile;
-        const float *C = a.carry + tbase * D + e0;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) S[e] = C[e];
-        for (int w = 0; w < wave; ++w) {
+    for (int e = 0; e < EPL; ++e) S[e] = Cin[e];
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        if (w < wave) {
             const int s0 = t0 + kBlk * w;
             const float gl = powi(gm, evict_steps(p0, s0, min(kBlk, n - s0), W));
-            const float *A = a.agg16 + (tbase * 4 + w) * D + e0;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) S[e] = gl * S[e] + A[e];
+            for (int e = 0; e < EPL; ++e) S[e] = gl * S[e] + Ain[w][e];
         }
     }
     __syncthreads();

@@ -513,13 +513,17 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
             const float sa = (float)Acol[(kBlk + t) * AS];
             return reach_ring ? xa : sa;
         };
-        // ring sum of tokens -R .. -1, then slide: + token t, - token t-R
+        // ring mean of tokens -R .. -1 (kept pre-divided by R), then slide:
+        // + token t, - token t-R; the field is kept pre-halved (F' = F / 2)
         float rs = 0.f;
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) {
             const float v = before(-1 - k);
             rs += k < R ? v : 0.f;
         }
+        rs *= invR;
+        F *= 0.5f;
+        const float hg = 0.5f * (1.f - g);
         for (int tg = 0; tg < 4; ++tg) {
             const int j0 = 16 * tg;
             if (j0 >= len) break;  // wave-uniform
@@ -533,12 +537,21 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
                 const float os = (float)Acol[(kBlk + t - R) * AS];
                 old[j] = (tg == 0 && t - R < 0) ? before(t - R) : os;
             }
+            if (j0 + kBlk <= len) {  // wave-uniform: a whole group of tokens
 #pragma unroll
-            for (int j = 0; j < kBlk; ++j) {
-                const bool ok = j0 + j < len;
-                rs = ok ? rs + (cur[j] - old[j]) : rs;
-                F = ok ? g * F + (1.f - g) * cur[j] : F;
-                Xw[j * XS + lane] = rs * invR + 0.5f * F;
+                for (int j = 0; j < kBlk; ++j) {
+                    rs = fmaf(cur[j] - old[j], invR, rs);
+                    F = fmaf(g, F, hg * cur[j]);
+                    Xw[j * XS + lane] = rs + F;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kBlk; ++j) {
+                    const bool ok = j0 + j < len;
+                    rs = ok ? fmaf(cur[j] - old[j], invR, rs) : rs;
+                    F = ok ? fmaf(g, F, hg * cur[j]) : F;
+                    Xw[j * XS + lane] = rs + F;
+                }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();

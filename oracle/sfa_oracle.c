@@ -55,7 +55,10 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
  *  - S starts at 0; at position p >= W exactly one key, the one at p-W,
  *    leaves the window and enters S; the token at p uses S after its own
  *    eviction, so window and S together account for keys 0..p exactly once;
- *  - S is per KV head (γ indexed by KV head), α per query head;
+ *  - S is per KV head (γ indexed by KV head), α per query head; with
+ *    s_per_query set, the other reading of "per-head γ": γ and S per query
+ *    head (every query head of a group folds the same evicted keys with its
+ *    own decay);
  *  - query head h reads KV head h / (Hq/Hkv);
  *  - scale <= 0 means 1/sqrt(d).
  *
@@ -65,7 +68,7 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
  *
  * Layouts: q [B,n,Hq,d]; k, v [B,n,Hkv,d]; out [B,n,Hq,d];
  * ring_k, ring_v [B,Hkv,W,d] (in/out); state [B,Hkv,d] (in/out);
- * gamma [Hkv]; alpha [Hq].
+ * gamma [Hkv]; alpha [Hq].  With s_per_query: state [B,Hq,d], gamma [Hq].
  * ------------------------------------------------------------------------ */
 
 /* key/value of position qpos for batch b, KV head G */
@@ -83,26 +86,28 @@ void oracle_prefill(const float *q, const float *k, const float *v,
                     const double *gamma, const double *alpha,
                     double *out, double *ring_k, double *ring_v, double *state,
                     const int32_t *pos0,
-                    int B, int n, int Hq, int Hkv, int d, int W, double scale) {
+                    int B, int n, int Hq, int Hkv, int d, int W, double scale, int s_per_query) {
     const int group = Hq / Hkv;
+    const int Hs = s_per_query ? Hq : Hkv; /* heads that own an S */
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
-    /* final S of each (b, KV head), written to state after the loop so that
+    /* final S of each (b, S head), written to state after the loop so that
      * every head reads the caller's ring/state as they were on entry */
-    double *final_S = (double *)calloc((size_t)B * Hkv * d, sizeof(double));
+    double *final_S = (double *)calloc((size_t)B * Hs * d, sizeof(double));
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b) {
         for (int h = 0; h < Hq; ++h) {
             const int G = h / group;
+            const int hs = s_per_query ? h : G; /* the head that owns this S */
             const int p0 = pos0 ? pos0[b] : 0;
-            const double g = gamma[G];
+            const double g = gamma[hs];
             double *S = (double *)malloc(sizeof(double) * d);
             double *o = (double *)malloc(sizeof(double) * d);
             double *tk = (double *)malloc(sizeof(double) * d);
             double *tv = (double *)malloc(sizeof(double) * d);
             double *sc = (double *)malloc(sizeof(double) * W);
             for (int e = 0; e < d; ++e)
-                S[e] = (p0 > 0) ? state[IDX4(0, b, G, e, B, Hkv, d)] : 0.0;
+                S[e] = (p0 > 0) ? state[IDX4(0, b, hs, e, B, Hs, d)] : 0.0;
 
             for (int t = 0; t < n; ++t) {
                 const int p = p0 + t;
@@ -138,8 +143,8 @@ void oracle_prefill(const float *q, const float *k, const float *v,
                 double *dst = out + IDX4(b, t, h, 0, n, Hq, d);
                 for (int e = 0; e < d; ++e) dst[e] = o[e] + alpha[h] * S[e];
             }
-            if (h % group == 0)
-                for (int e = 0; e < d; ++e) final_S[IDX4(0, b, G, e, B, Hkv, d)] = S[e];
+            if (s_per_query || h % group == 0)
+                for (int e = 0; e < d; ++e) final_S[IDX4(0, b, hs, e, B, Hs, d)] = S[e];
             free(S); free(o); free(tk); free(tv); free(sc);
         }
     }
@@ -158,9 +163,10 @@ void oracle_prefill(const float *q, const float *k, const float *v,
                 const float *sv = v + IDX4(b, p - p0, G, 0, n, Hkv, d);
                 for (int e = 0; e < d; ++e) { rk[e] = sk[e]; rv[e] = sv[e]; }
             }
-            for (int e = 0; e < d; ++e)
-                state[IDX4(0, b, G, e, B, Hkv, d)] = final_S[IDX4(0, b, G, e, B, Hkv, d)];
         }
+        for (int hs = 0; hs < Hs; ++hs)
+            for (int e = 0; e < d; ++e)
+                state[IDX4(0, b, hs, e, B, Hs, d)] = final_S[IDX4(0, b, hs, e, B, Hs, d)];
     }
     free(final_S);
 }
@@ -178,13 +184,15 @@ void oracle_prefill(const float *q, const float *k, const float *v,
  *
  * Layouts: q [L,B,Hq,d]; k_new, v_new [L,B,Hkv,d]; ring_k, ring_v
  * [L,B,Hkv,W,d] (in/out); state [L,B,Hkv,d] (in/out); pos [B];
- * gamma [L,Hkv]; alpha [L,Hq]; out [L,B,Hq,d].
+ * gamma [L,Hkv]; alpha [L,Hq]; out [L,B,Hq,d].  With s_per_query (γ and S per
+ * query head, see oracle_prefill): state [L,B,Hq,d], gamma [L,Hq]; every query
+ * head folds the same evicted key into its own S.
  * ------------------------------------------------------------------------ */
 void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                         double *ring_k, double *ring_v, double *state,
                         const int32_t *pos, const double *gamma, const double *alpha,
                         double *out, int L, int B, int Hq, int Hkv, int d, int W,
-                        double scale) {
+                        double scale, int s_per_query) {
     const int group = Hq / Hkv;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
     if (W > 64) return; /* the ring of [P1] §2.2 has k = 16 slots */
@@ -195,16 +203,22 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
             for (int G = 0; G < Hkv; ++G) {
                 const int p = pos[b];
                 const int s = p % W;
-                const double g = gamma[(size_t)l * Hkv + G];
                 const size_t unit = ((size_t)l * B + b) * Hkv + G;
-                double *S = state + unit * d;
                 double *rk = ring_k + unit * W * d;
                 double *rv = ring_v + unit * W * d;
                 const float *kn = k_new + unit * d;
                 const float *vn = v_new + unit * d;
 
-                if (p >= W)
-                    for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
+                /* the evicted key (old contents of slot s) enters every S of the unit */
+                const int n_s = s_per_query ? group : 1;
+                for (int i = 0; i < n_s; ++i) {
+                    const size_t hs = s_per_query ? ((size_t)l * B + b) * Hq + (size_t)G * group + i : unit;
+                    const double g = s_per_query ? gamma[(size_t)l * Hq + (size_t)G * group + i]
+                                                 : gamma[(size_t)l * Hkv + G];
+                    double *S = state + hs * d;
+                    if (p >= W)
+                        for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
+                }
                 for (int e = 0; e < d; ++e) {
                     rk[(size_t)s * d + e] = kn[e];
                     rv[(size_t)s * d + e] = vn[e];
@@ -226,6 +240,7 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                     for (int j = 0; j < nvalid; ++j) { sc[j] = exp(sc[j] - m); den += sc[j]; }
                     double *dst = out + (((size_t)l * B + b) * Hq + h) * d;
                     const double a = alpha[(size_t)l * Hq + h];
+                    const double *S = state + (s_per_query ? ((size_t)l * B + b) * Hq + h : unit) * d;
                     for (int e = 0; e < d; ++e) {
                         double o = 0.0;
                         for (int j = 0; j < nvalid; ++j) o += (sc[j] / den) * rv[(size_t)j * d + e];

@@ -18,22 +18,28 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "sfa_oracle.c")
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 
-DECODE_EVICT_THEN_WRITE = """                if (p >= W)
-                    for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
+DECODE_EVICT_THEN_WRITE = """                    if (p >= W)
+                        for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
+                }
                 for (int e = 0; e < d; ++e) {
                     rk[(size_t)s * d + e] = kn[e];
                     rv[(size_t)s * d + e] = vn[e];
                 }
 """
-DECODE_WRITE_THEN_EVICT = """                for (int e = 0; e < d; ++e) {
-                    rk[(size_t)s * d + e] = kn[e];
-                    rv[(size_t)s * d + e] = vn[e];
+DECODE_WRITE_THEN_EVICT = """                    for (int e = 0; e < d; ++e) {
+                        rk[(size_t)s * d + e] = kn[e];
+                        rv[(size_t)s * d + e] = vn[e];
+                    }
+                    if (p >= W)
+                        for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
                 }
-                if (p >= W)
-                    for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
 """
 
 MUTANTS = {
+    "per_query_gamma_of_kv_head": ("const double g = gamma[hs];", "const double g = gamma[G];"),
+    "per_query_state_of_first_head_only": ("if (s_per_query || h % group == 0)", "if (h % group == 0)"),
+    "per_query_decode_one_gamma": ("gamma[(size_t)l * Hq + (size_t)G * group + i]",
+                                   "gamma[(size_t)l * Hq + (size_t)G * group]"),
     "window_one_too_wide": ("const int lo = (p - W + 1 > 0) ? p - W + 1 : 0;",
                             "const int lo = (p - W > 0) ? p - W : 0;"),
     "evicts_wrong_key": ("kv_row(k, ring_k, b, G, p - W, p0", "kv_row(k, ring_k, b, G, p - W + 1, p0"),

@@ -478,3 +478,114 @@ def test_enhance_brute_force_tiny():
             w /= w.sum()
             e = np.clip(rm + 0.5 * F + 0.5 * (w @ P[l]), -clip, clip)
             np.testing.assert_allclose(out[l, t], a + al * e, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P12: the other reading of "per-head γ" (γ and S per query head)
+# --------------------------------------------------------------------------
+def _brute_force_per_query(q, k, v, gamma_q, alpha, W, scale):
+    """Masked dense attention plus, per query head h, the power sum of its KV
+    head's evicted keys with γ_h."""
+    B, n, Hq, d = q.shape
+    g = Hq // k.shape[2]
+    out = np.zeros((B, n, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            K = k[b, :, h // g].astype(np.float64)
+            V = v[b, :, h // g].astype(np.float64)
+            S = _ewma_closed_form(K, gamma_q[h], W)
+            s = scale * (q[b, :, h].astype(np.float64) @ K.T)
+            s = np.where(_band(n, W), s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            out[b, :, h] = p @ V + alpha[h] * S
+    return out
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_per_query_gamma_brute_force_tiny(case):
+    r = np.random.default_rng(100 + case)
+    W = int(r.integers(1, 17))
+    n = int(r.integers(1, 41))
+    d = int(r.integers(1, 9))
+    Hkv = int(r.integers(1, 3))
+    Hq = Hkv * int(r.integers(2, 4))
+    B = int(r.integers(1, 3))
+    q = r.standard_normal((B, n, Hq, d)).astype(np.float32)
+    k = r.standard_normal((B, n, Hkv, d)).astype(np.float32)
+    v = r.standard_normal((B, n, Hkv, d)).astype(np.float32)
+    gamma_q = r.uniform(0.0, 0.99, Hq)
+    alpha = r.uniform(-0.5, 0.5, Hq)
+    scale = float(r.uniform(0.1, 1.0))
+    out, _, _, st = oracle.prefill(q, k, v, gamma_q, alpha, W, scale, s_per_query=True)
+    np.testing.assert_allclose(out, _brute_force_per_query(q, k, v, gamma_q, alpha, W, scale),
+                               rtol=1e-11, atol=1e-12)
+    # the final state of every query head is its power sum at the last token
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            K = k[b, :, h // g].astype(np.float64)
+            last = _ewma_closed_form(K, gamma_q[h], W)[n - 1]
+            np.testing.assert_allclose(st[b, h], last, rtol=1e-11, atol=1e-12)
+
+
+def test_per_query_gamma_equal_within_group_is_kv_mode():
+    """γ_h equal to γ_G for every query head of group G: the same outputs, and
+    every query head's S equal to its KV head's S (prefill and decode)."""
+    B, n, Hq, Hkv, d, W = 2, 45, 6, 2, 8, 16
+    g = Hq // Hkv
+    q, k, v = _rand((B, n, Hq, d)), _rand((B, n, Hkv, d)), _rand((B, n, Hkv, d))
+    gamma, alpha = RNG.uniform(0.5, 0.99, Hkv), RNG.uniform(0, 0.5, Hq)
+    a = oracle.prefill(q, k, v, gamma, alpha, W)
+    b_ = oracle.prefill(q, k, v, np.repeat(gamma, g), alpha, W, s_per_query=True)
+    np.testing.assert_array_equal(a[0], b_[0])
+    np.testing.assert_array_equal(np.repeat(a[3], g, axis=1), b_[3])
+    L = 2
+    dq, dk, dv = _rand((L, B, Hq, d)), _rand((L, B, Hkv, d)), _rand((L, B, Hkv, d))
+    rk, rv, st = _rand((L, B, Hkv, W, d)), _rand((L, B, Hkv, W, d)), _rand((L, B, Hkv, d))
+    pos = np.array([3, 40], dtype=np.int32)
+    gl, al = RNG.uniform(0.5, 0.99, (L, Hkv)), RNG.uniform(0, 0.5, (L, Hq))
+    x = oracle.decode_step(dq, dk, dv, rk, rv, st, pos, gl, al)
+    y = oracle.decode_step(dq, dk, dv, rk, rv, np.repeat(st, g, axis=2), pos, np.repeat(gl, g, axis=1),
+                           al, s_per_query=True)
+    np.testing.assert_array_equal(x[0], y[0])
+    np.testing.assert_array_equal(np.repeat(x[3], g, axis=2), y[3])
+    assert np.array_equal(x[1], y[1]) and np.array_equal(x[2], y[2])
+
+
+@pytest.mark.parametrize("n,m,W", [(20, 5, 16), (0, 9, 4), (15, 2, 16), (7, 7, 1)])
+def test_per_query_prefill_then_decode_equals_longer_prefill(n, m, W):
+    """P7 with γ and S per query head."""
+    B, Hq, Hkv, d = 2, 6, 2, 8
+    N = n + m
+    q, k, v = _rand((B, N, Hq, d)), _rand((B, N, Hkv, d)), _rand((B, N, Hkv, d))
+    gamma, alpha = RNG.uniform(0.3, 0.99, Hq), RNG.uniform(0, 0.5, Hq)
+    full, frk, frv, fst = oracle.prefill(q, k, v, gamma, alpha, W, s_per_query=True)
+    if n > 0:
+        _, rk, rv, st = oracle.prefill(q[:, :n], k[:, :n], v[:, :n], gamma, alpha, W, s_per_query=True)
+    else:
+        rk, rv, st = np.zeros((B, Hkv, W, d)), np.zeros((B, Hkv, W, d)), np.zeros((B, Hq, d))
+    for i in range(m):
+        t = n + i
+        o, rk, rv, st = oracle.decode_step(q[None, :, t], k[None, :, t], v[None, :, t],
+                                           rk[None], rv[None], st[None],
+                                           np.full(B, t, dtype=np.int32), gamma[None],
+                                           alpha[None], s_per_query=True)
+        rk, rv, st = rk[0], rv[0], st[0]
+        np.testing.assert_allclose(o[0], full[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st, fst, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("n1,n2,W", [(20, 13, 16), (40, 3, 4)])
+def test_per_query_continuation_equals_single_prefill(n1, n2, W):
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    N = n1 + n2
+    q, k, v = _rand((B, N, Hq, d)), _rand((B, N, Hkv, d)), _rand((B, N, Hkv, d))
+    gamma, alpha = RNG.uniform(0.3, 0.99, Hq), RNG.uniform(0, 0.5, Hq)
+    full, frk, frv, fst = oracle.prefill(q, k, v, gamma, alpha, W, s_per_query=True)
+    o1, rk, rv, st = oracle.prefill(q[:, :n1], k[:, :n1], v[:, :n1], gamma, alpha, W, s_per_query=True)
+    o2, rk, rv, st = oracle.prefill(q[:, n1:], k[:, n1:], v[:, n1:], gamma, alpha, W,
+                                    ring_k=rk, ring_v=rv, state=st,
+                                    pos0=np.full(B, n1, dtype=np.int32), s_per_query=True)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), full, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st, fst, rtol=1e-12, atol=1e-14)

@@ -137,6 +137,27 @@ int sfa_prefill_part(int parts, const void *q, const void *k, const void *v,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sfa_prefill_qh -- sfa_prefill under the other reading of "per-head γ" with
+ * grouped-query attention: γ and the far-field state S belong to each QUERY
+ * head.  Every query head of a group folds the same evicted keys (those of its
+ * KV head) into its own S with its own decay; the near field and the ring are
+ * those of sfa_prefill.  ([P1] §2.1 far-field and fusion equations; the
+ * configs give "per-head γ" without saying which heads.)
+ *  gamma    [Hq] fp32.
+ *  state    [B,Hq,d] fp32 (written; read first when pos0 != NULL).
+ *  workspace at least sfa_prefill_workspace_size(B, n, Hq, d) bytes (the scan
+ *           keeps one chain per query head).
+ * Every other argument, layout and error code is that of sfa_prefill.
+ */
+int sfa_prefill_qh(const void *q, const void *k, const void *v,
+                   const float *gamma, const float *alpha,
+                   void *out, void *ring_k, void *ring_v, float *state,
+                   const int32_t *pos0,
+                   int B, int n, int Hq, int Hkv, int d, int window, float scale,
+                   int in_dtype, int out_dtype,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * sfa_decode_step -- one generated token for L layers at once.
  * (First page, section 2.1 equations with the constant-memory k-slot ring of
  * section 2.2.)
@@ -163,6 +184,19 @@ int sfa_decode_step(const void *q, const void *k_new, const void *v_new,
                     const int32_t *pos, const float *gamma, const float *alpha,
                     void *out, int L, int B, int Hq, int Hkv, int d, int window,
                     float scale, int in_dtype, int out_dtype, void *stream);
+
+/*
+ * sfa_decode_step_qh -- sfa_decode_step with γ and S per query head (see
+ * sfa_prefill_qh): when the key of position pos-W leaves the window it enters
+ * the S of every query head of its group, each with that head's decay.
+ *  gamma  [L,Hq] fp32;  state [L,B,Hq,d] fp32 (in/out).
+ * Every other argument, layout and error code is that of sfa_decode_step.
+ */
+int sfa_decode_step_qh(const void *q, const void *k_new, const void *v_new,
+                       void *ring_k, void *ring_v, float *state,
+                       const int32_t *pos, const float *gamma, const float *alpha,
+                       void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale,
+                       int in_dtype, int out_dtype, void *stream);
 
 /*
  * Workspace bytes sfa_enhance needs for (L, T, H): per-chunk fp32 aggregates

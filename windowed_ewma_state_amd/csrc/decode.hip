@@ -81,7 +81,8 @@ template <typename T> struct Vec<T, 2> {
     }
 };
 
-template <typename TIn, typename TOut, int D>
+// QH: γ and S per query head (state [L,B,Hq,d], gamma [L,Hq])
+template <typename TIn, typename TOut, int D, bool QH>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     constexpr int EPL = D / kWave;
     __shared__ float4 P_lds[kUnitsPerBlock][16][4];  // [unit][head in tile][slots/4]
@@ -115,7 +116,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 
     // ---- issue the unit's loads -------------------------------------------
     float S[EPL], kev[EPL];
-    Vec<float, EPL>::load(S_ptr + e0, S);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) S[e] = kev[e] = 0.f;
+    if constexpr (!QH) Vec<float, EPL>::load(S_ptr + e0, S);
     const bool evict = p >= W;
     if (evict) Vec<TIn, EPL>::load(ringK + (long)s * D + e0, kev);
 
@@ -132,8 +135,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     }
 
     // ---- far field: the key of position p-W leaves the window -------------
-    const float gm = a.gamma[(long)l * a.Hkv + G];
-    if (evict) {
+    if (!QH && evict) {
+        const float gm = a.gamma[(long)l * a.Hkv + G];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kev[e];
     }
@@ -182,15 +185,28 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) o[e] = fmaf(P[j], vrow[j][e], o[e]);
             const float al = alpha[ht + hh];
+            float Sh[EPL];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = fmaf(al, S[e], o[e]);
+            for (int e = 0; e < EPL; ++e) Sh[e] = S[e];
+            if constexpr (QH) {  // this query head's own S, evicted key folded in
+                const long hs = lb * a.Hq + (long)G * group + ht + hh;
+                Vec<float, EPL>::load(a.state + hs * D + e0, Sh);
+                if (evict) {
+                    const float gh = a.gamma[(long)l * a.Hq + (long)G * group + ht + hh];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) Sh[e] = gh * Sh[e] + (1.f - gh) * kev[e];
+                }
+                Vec<float, EPL>::store(a.state + hs * D + e0, Sh);
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = fmaf(al, Sh[e], o[e]);
             Vec<TOut, EPL>::store(outg + (long)(ht + hh) * D + e0, o);
         }
         __builtin_amdgcn_wave_barrier();
     }
 
     // ---- cache update (after every read of the unit's ring) -----------------
-    Vec<float, EPL>::store(S_ptr + e0, S);
+    if constexpr (!QH) Vec<float, EPL>::store(S_ptr + e0, S);
     Vec<TIn, EPL>::copy(ringK + (long)s * D + e0, kn + e0);
     Vec<TIn, EPL>::copy(ringV + (long)s * D + e0, vn + e0);
 }
@@ -227,7 +243,7 @@ struct UnitLoads {
     int p;
 };
 
-template <int D>
+template <int D, bool QH>
 __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoads<D> &u, int lane) {
     constexpr int EPL = D / kWave;
     const int q4 = lane >> 4, c16 = lane & 15;
@@ -270,9 +286,11 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     }
     // far-field state, evicted key, new key/value (e-pair layout)
     const int e0 = lane * EPL;
-    const float *S_ptr = a.state + (long)unit * D + e0;
+    if constexpr (!QH) {  // (per query head, the compute step reads its heads' S)
+        const float *S_ptr = a.state + (long)unit * D + e0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) u.S[e] = S_ptr[e];
+        for (int e = 0; e < EPL; ++e) u.S[e] = S_ptr[e];
+    }
     const __bf16 *kev = ringK + (long)s * D + e0;  // position p-W when p >= W
     if (EPL == 2) {
         const uint32_t kw = *reinterpret_cast<const uint32_t *>(kev);
@@ -288,7 +306,7 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     }
 }
 
-template <typename TOut, int D>
+template <typename TOut, int D, bool QH>
 __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, const UnitLoads<D> &u, int lane,
                                              __bf16 *vt, float *sl) {
     constexpr int EPL = D / kWave;
@@ -304,12 +322,32 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
         const int s = p % W;
         const int nvalid = (p >= W - 1) ? W : p + 1;
         // far field: the key of position p-W leaves the window
-        const float gm = a.gamma[(long)l * a.Hkv + G];
         float S[EPL];
+        if constexpr (!QH) {
+            const float gm = a.gamma[(long)l * a.Hkv + G];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * u.kev[e] : u.S[e];
+            for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * u.kev[e] : u.S[e];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) sl[e0 + e] = S[e];
+            for (int e = 0; e < EPL; ++e) sl[e0 + e] = S[e];
+        }
+        // per query head: lane (q4, c16) reads the S of head c16 and the evicted
+        // key at its own epilogue positions d = 32k + 8q4 + 4half + i
+        const int hc = c16 < group ? c16 : group - 1;
+        f32x4 Sq[QH ? D / 32 : 1][2];
+        u32x2 kq[QH ? D / 32 : 1][2];
+        float gq = 0.f;
+        if constexpr (QH) {
+            const float *Sg = a.state + ((long)lb * a.Hq + (long)G * group + hc) * D + 8 * q4;
+            const __bf16 *kg = reinterpret_cast<const __bf16 *>(a.ring_k) + ((long)unit * W + s) * D + 8 * q4;
+#pragma unroll
+            for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    Sq[k][half] = *reinterpret_cast<const f32x4 *>(Sg + 32 * k + 4 * half);
+                    kq[k][half] = *reinterpret_cast<const u32x2 *>(kg + 32 * k + 4 * half);
+                }
+            gq = a.gamma[(long)l * a.Hq + (long)G * group + hc];
+        }
         // V^T tile: row = head-dim element, 16 slots per row; consecutive
         // lanes write consecutive dwords (slot pairs)
         const int m = lane & 7, c = lane >> 3;
@@ -368,7 +406,19 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
                 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, Ph, o, 0, 0, 0);
                 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, Pl, o, 0, 0, 0);
-                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sl[32 * k + 8 * q4 + 4 * half]);
+                f32x4 s4;
+                if constexpr (QH) {
+                    s4 = Sq[k][half];
+                    if (p >= W) {
+                        const u32x2 kw = kq[k][half];
+                        const float kv[4] = {bf16_lo(kw[0]), bf16_hi(kw[0]), bf16_lo(kw[1]), bf16_hi(kw[1])};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s4[i] = gq * s4[i] + (1.f - gq) * kv[i];
+                    }
+                    Sq[k][half] = s4;
+                } else {
+                    s4 = *reinterpret_cast<const f32x4 *>(&sl[32 * k + 8 * q4 + 4 * half]);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ov[4 * half + i] = fmaf(al, s4[i], o[i]);
             }
@@ -385,15 +435,29 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
             }
         }
         // cache update (every read of this unit's ring is done)
-        float *S_ptr = a.state + (long)unit * D + e0;
+        if constexpr (QH) {
+            if (head_ok) {
+                float *Sg = a.state + ((long)lb * a.Hq + (long)G * group + c16) * D + 8 * q4;
+#pragma unroll
+                for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+                        *reinterpret_cast<f32x4 *>(Sg + 32 * k + 4 * half) = Sq[k][half];
+            }
+        } else {
+            float *S_ptr = a.state + (long)unit * D + e0;
+            if constexpr (EPL == 2) {
+                *reinterpret_cast<float2 *>(S_ptr) = make_float2(S[0], S[EPL - 1]);
+            } else {
+                S_ptr[0] = S[0];
+            }
+        }
         __bf16 *ringK = reinterpret_cast<__bf16 *>(a.ring_k) + ((long)unit * W + s) * D + e0;
         __bf16 *ringV = reinterpret_cast<__bf16 *>(a.ring_v) + ((long)unit * W + s) * D + e0;
         if constexpr (EPL == 2) {
-            *reinterpret_cast<float2 *>(S_ptr) = make_float2(S[0], S[EPL - 1]);
             *reinterpret_cast<uint32_t *>(ringK) = u.kn;
             *reinterpret_cast<uint32_t *>(ringV) = u.vn;
         } else {
-            S_ptr[0] = S[0];
             *reinterpret_cast<uint16_t *>(ringK) = (uint16_t)u.kn;
             *reinterpret_cast<uint16_t *>(ringV) = (uint16_t)u.vn;
         }
@@ -401,7 +465,7 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
     }
 }
 
-template <typename TOut, int D>
+template <typename TOut, int D, bool QH>
 __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
     constexpr int VTS = kMaxWindow + 4;  // V^T row stride (bf16): 16 slots + pad
     __shared__ __attribute__((aligned(16))) __bf16 Vt[4][D * VTS];
@@ -418,14 +482,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
     // two register buffers in turn: the next unit's loads are in flight while
     // the current one computes
     UnitLoads<D> A, Bf;
-    if (unit < n_units) unit_load<D>(a, unit, A, lane);
+    if (unit < n_units) unit_load<D, QH>(a, unit, A, lane);
     while (unit < n_units) {
-        if (unit + stride < n_units) unit_load<D>(a, unit + stride, Bf, lane);
-        unit_compute<TOut, D>(a, unit, A, lane, vt, sl);
+        if (unit + stride < n_units) unit_load<D, QH>(a, unit + stride, Bf, lane);
+        unit_compute<TOut, D, QH>(a, unit, A, lane, vt, sl);
         unit += stride;
         if (unit >= n_units) break;
-        if (unit + stride < n_units) unit_load<D>(a, unit + stride, A, lane);
-        unit_compute<TOut, D>(a, unit, Bf, lane, vt, sl);
+        if (unit + stride < n_units) unit_load<D, QH>(a, unit + stride, A, lane);
+        unit_compute<TOut, D, QH>(a, unit, Bf, lane, vt, sl);
         unit += stride;
     }
 }
@@ -455,21 +519,26 @@ hipError_t launch_persistent(K kernel, const DecodeArgs &a, long units, hipStrea
     return hipGetLastError();
 }
 
-template <typename TIn, typename TOut>
-hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
+template <typename TIn, typename TOut, bool QH>
+hipError_t launch_q(const DecodeArgs &a, hipStream_t stream) {
     const long units = (long)a.L * a.B * a.Hkv;
     if constexpr (std::is_same<TIn, __bf16>::value) {
         if (a.group <= 16) {
-            if (a.d == 128) return launch_persistent(k_decode_mfma<TOut, 128>, a, units, stream);
-            return launch_persistent(k_decode_mfma<TOut, 64>, a, units, stream);
+            if (a.d == 128) return launch_persistent(k_decode_mfma<TOut, 128, QH>, a, units, stream);
+            return launch_persistent(k_decode_mfma<TOut, 64, QH>, a, units, stream);
         }
     }
     const dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock));
     if (a.d == 128)
-        hipLaunchKernelGGL((k_decode<TIn, TOut, 128>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_decode<TIn, TOut, 128, QH>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_decode<TIn, TOut, 64>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_decode<TIn, TOut, 64, QH>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
+    return a.s_per_query ? launch_q<TIn, TOut, true>(a, stream) : launch_q<TIn, TOut, false>(a, stream);
 }
 
 }  // namespace

@@ -67,17 +67,18 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     const int tiles_per_bg = a.ntiles;
     // chain fastest: the waves of a workgroup take the same tile of consecutive
     // (b, KV head) chains, i.e. neighbouring 256-byte pieces of the same rows
-    const int nbg = a.B * a.Hkv;
+    const int nbg = a.B * a.Hs;  // scan chains (b, S head)
     const int gt = blockIdx.x * 4 + wave;
     if (gt >= nbg * tiles_per_bg) return;
     const int tile = gt / nbg, bg = gt - tile * nbg;
-    const int b = bg / a.Hkv, G = bg % a.Hkv;
+    const int b = bg / a.Hs, hs = bg % a.Hs;
+    const int G = a.s_per_query ? hs / a.group : hs;  // the KV head whose keys the chain folds
     const int n = a.n, W = a.W;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
-    const float gm = a.gamma[G];
+    const float gm = a.gamma[hs];
     const long row_stride = (long)a.Hkv * D;
     const TIn *Kbg = reinterpret_cast<const TIn *>(a.k) + ((long)b * n * a.Hkv + G) * D;
-    const TIn *ringK = a.pos0 ? reinterpret_cast<const TIn *>(a.ring_k) + (long)bg * W * D : nullptr;
+    const TIn *ringK = a.pos0 ? reinterpret_cast<const TIn *>(a.ring_k) + ((long)b * a.Hkv + G) * W * D : nullptr;
     const int blk = lane / LPB, c0 = lane % LPB;
     const int tb = tile * kTile + kBlk * blk;
     const bool lane_ok = c0 < CPR;  // d = 64 bf16 has 8 chunks per row: half the lanes idle
@@ -179,10 +180,10 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
     const int bg = blockIdx.x / cblocks;
     const int e = (blockIdx.x % cblocks) * kCarryCols + threadIdx.x % kCarryCols;
     const int part = threadIdx.x / kCarryCols;
-    const int b = bg / a.Hkv, G = bg % a.Hkv;
+    const int b = bg / a.Hs, hs = bg % a.Hs;
     const int n = a.n, W = a.W, nt = a.ntiles;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
-    const float gm = a.gamma[G];
+    const float gm = a.gamma[hs];
     const float S_init = (a.pos0 && p0 > 0) ? a.state[(long)bg * D + e] : 0.f;
     const float g64 = powi(gm, kTile);
 
@@ -275,7 +276,9 @@ __device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float *v) {
     *reinterpret_cast<u32x4 *>(p) = w;
 }
 
-template <typename TIn, typename TOut, int D>
+// QH: γ and S per query head (scan chains (b, query head)); each head's S tile
+// is rebuilt in the head loop from its carry and the wave's evicted keys.
+template <typename TIn, typename TOut, int D, bool QH>
 __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     constexpr bool kBf16 = std::is_same<TIn, __bf16>::value;
     constexpr int EPL = D / kWave;
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     const int n = a.n, W = a.W, group = a.group;
     const int t0 = tile * kTile;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
-    const float gm = a.gamma[G];
+    const float gm = QH ? 0.f : a.gamma[G];  // KV-head decay (QH reads its heads' own)
     const int tb = t0 + kBlk * wave;  // this wave's 16 tokens
     const int tok = tb + c16;         // this lane's token in the MFMA layouts
     const bool tok_ok = tok < n;
@@ -343,19 +346,24 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // the S carried into the tile and the aggregates of this wave's earlier
     // blocks (read in step 2) go out with the queries, ahead of the staging
     const int e0 = lane * EPL;
-    float Cin[EPL], Ain[3][EPL];
-    {
-        const long tbase = (long)bg * a.ntiles + tile;
+    // carry of scan chain `chain` at this tile and the aggregates of the
+    // wave's earlier blocks
+    auto carry_loads = [&](long chain, float *Cx, float (*Ax)[EPL]) {
+        const long tbase = chain * a.ntiles + tile;
         const float *C = a.carry + tbase * D + e0;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) Cin[e] = C[e];
+        for (int e = 0; e < EPL; ++e) Cx[e] = C[e];
 #pragma unroll
         for (int w = 0; w < 3; ++w) {
             const float *A = a.agg16 + (tbase * 4 + w) * D + e0;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) Ain[w][e] = w < wave ? A[e] : 0.f;
+            for (int e = 0; e < EPL; ++e) Ax[w][e] = w < wave ? A[e] : 0.f;
         }
-    }
+    };
+    // QH: chain of query head h of this group
+    const long chain0 = QH ? (long)b * a.Hq + (long)G * group : (long)bg;
+    float Cin[EPL], Ain[3][EPL];
+    carry_loads(chain0, Cin, Ain);
 
     // ---- (1) stage K rows (row-major) and V (transposed) ---------------------
     for (int idx = tid; idx < kRows * CPR; idx += 256) {
@@ -410,38 +418,81 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
         }
     }
 
-    // ---- (2) S just before this wave's 16-token block -----------------------
-    float S[EPL];
+    // ---- (2) S just before this wave's 16-token block (KV heads) ------------
+    // S_{block start} = carry through the wave's earlier blocks of the tile
+    auto block_start = [&](float g, const float *Cx, float (*Ax)[EPL], float *Sx) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) S[e] = Cin[e];
+        for (int e = 0; e < EPL; ++e) Sx[e] = Cx[e];
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
-        if (w < wave) {
-            const int s0 = t0 + kBlk * w;
-            const float gl = powi(gm, evict_steps(p0, s0, min(kBlk, n - s0), W));
+        for (int w = 0; w < 3; ++w) {
+            if (w < wave) {
+                const int s0 = t0 + kBlk * w;
+                const float gl = powi(g, evict_steps(p0, s0, min(kBlk, n - s0), W));
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) S[e] = gl * S[e] + Ain[w][e];
+                for (int e = 0; e < EPL; ++e) Sx[e] = gl * Sx[e] + Ax[w][e];
+            }
         }
-    }
-    __syncthreads();
-
-    // ---- (3) EWMA through the block: S_t after token t's own eviction ---------
+    };
     float *Sw = Sb[wave];
+    // QH: the keys evicted by this wave's 16 tokens, kept in registers (the K
+    // staging area is reused in the head loop)
+    float kev[QH ? kBlk : 1][EPL];
+    if constexpr (!QH) {
+        float S[EPL];
+        block_start(gm, Cin, Ain, S);
+        __syncthreads();
+
+        // ---- (3) EWMA through the block: S_t after token t's own eviction -----
 #pragma unroll
-    for (int j = 0; j < kBlk; ++j) {
-        const int t = tb + j;
-        if (t < n && p0 + t >= W) {
-            // token t - W sits in staged row (t - W) - (t0 - 16)
-            const TIn *kr = &Klds[(kBlk * wave + j + kMaxWindow - W) * KS + e0];
-            float kv[EPL];
-            load_epl<TIn, EPL>(kr, kv);
+        for (int j = 0; j < kBlk; ++j) {
+            const int t = tb + j;
+            if (t < n && p0 + t >= W) {
+                // token t - W sits in staged row (t - W) - (t0 - 16)
+                const TIn *kr = &Klds[(kBlk * wave + j + kMaxWindow - W) * KS + e0];
+                float kv[EPL];
+                load_epl<TIn, EPL>(kr, kv);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kv[e];
+                for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kv[e];
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) Sw[j * SS + e0 + e] = S[e];
         }
+    } else {
+        __syncthreads();
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) Sw[j * SS + e0 + e] = S[e];
+        for (int j = 0; j < kBlk; ++j)
+            load_epl<TIn, EPL>(&Klds[(kBlk * wave + j + kMaxWindow - W) * KS + e0], kev[j]);
     }
     __syncthreads();
+    // QH: S tile of query head h (its carry in Cin/Ain) into Sw; the next
+    // head's carry loads go out here
+    auto head_S = [&](int h) {
+        if constexpr (QH) {
+            const float gh = a.gamma[chain0 - (long)b * a.Hq + h];
+            float Cx[EPL], Ax[3][EPL], S[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) Cx[e] = Cin[e];
+#pragma unroll
+            for (int w = 0; w < 3; ++w)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) Ax[w][e] = Ain[w][e];
+            if (h + 1 < group) carry_loads(chain0 + h + 1, Cin, Ain);
+            block_start(gh, Cx, Ax, S);
+#pragma unroll
+            for (int j = 0; j < kBlk; ++j) {
+                const int t = tb + j;
+                if (t < n && p0 + t >= W) {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) S[e] = gh * S[e] + (1.f - gh) * kev[j][e];
+                }
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) Sw[j * SS + e0 + e] = S[e];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    };
 
     // ---- (4) score-validity mask -------------------------------------------------
     // element T*4+i is key (tb-16) + 16T + 4*q4 + i for token tb + c16; key tiles
@@ -481,6 +532,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             for (int hh = 0; hh < kQSlots; ++hh) {
                 const int h = h0 + hh;
                 if (h >= group) continue;  // unrolled: keeps Qc indices static
+                head_S(h);
                 // row layout -> LDS tile -> B operands (lane: token c16, 8 elements)
 #pragma unroll
                 for (int j = 0; j < QLD; ++j)
@@ -586,6 +638,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
                 Kc[T][u] = *reinterpret_cast<const float4 *>(
                     &Klds[(kBlk * wave + 16 * T + c16) * KS + 16 * u + 4 * q4]);
         for (int hh = 0; hh < group; ++hh) {
+            head_S(hh);
             f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
             for (int u = 0; u < D / 16; ++u) {
@@ -672,11 +725,15 @@ template <typename TIn, typename TOut, int D>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t stream, int parts) {
     const unsigned tiles = (unsigned)(a.B * a.Hkv * a.ntiles);
     if (parts & kPrefillScan) {
-        hipLaunchKernelGGL((k_ewma_agg<TIn, D>), dim3((tiles + 3) / 4), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(k_ewma_carry, dim3(a.B * a.Hkv * (D / kCarryCols)), dim3(1024), 0, stream, a);
+        const unsigned scan_tiles = (unsigned)(a.B * a.Hs * a.ntiles);
+        hipLaunchKernelGGL((k_ewma_agg<TIn, D>), dim3((scan_tiles + 3) / 4), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(k_ewma_carry, dim3(a.B * a.Hs * (D / kCarryCols)), dim3(1024), 0, stream, a);
     }
     if (parts & kPrefillAttend) {
-        hipLaunchKernelGGL((k_window_attn<TIn, TOut, D>), dim3(tiles), dim3(256), 0, stream, a);
+        if (a.s_per_query)
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, true>), dim3(tiles), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, false>), dim3(tiles), dim3(256), 0, stream, a);
         if (a.pos0 && a.ring_k)
             hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
     }

@@ -41,20 +41,14 @@ size_t sfa_prefill_workspace_size(int B, int n, int Hkv, int d) {
     return sfa::prefill_workspace_bytes(B, n, Hkv, d);
 }
 
-int sfa_prefill(const void *q, const void *k, const void *v, const float *gamma, const float *alpha,
-                void *out, void *ring_k, void *ring_v, float *state, const int32_t *pos0, int B,
-                int n, int Hq, int Hkv, int d, int window, float scale, int in_dtype, int out_dtype,
-                void *workspace, size_t workspace_bytes, void *stream) {
-    return sfa_prefill_part(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, q, k, v, gamma, alpha, out, ring_k,
-                            ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype, out_dtype,
-                            workspace, workspace_bytes, stream);
-}
+namespace {
 
-int sfa_prefill_part(int parts, const void *q, const void *k, const void *v, const float *gamma,
-                     const float *alpha, void *out, void *ring_k, void *ring_v, float *state,
-                     const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
-                     float scale, int in_dtype, int out_dtype, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+// one prefill call; s_per_query selects γ and S per query head (Hs = Hq)
+int prefill_impl(int parts, int s_per_query, const void *q, const void *k, const void *v,
+                 const float *gamma, const float *alpha, void *out, void *ring_k, void *ring_v,
+                 float *state, const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
+                 float scale, int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes,
+                 void *stream) {
     if (parts < 1 || parts > (SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND)) return SFA_ERR_INVALID_ARG;
     if (B < 0 || n < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return SFA_ERR_INVALID_ARG;
     if (window < 1 || window > SFA_MAX_WINDOW) return SFA_ERR_INVALID_ARG;
@@ -68,7 +62,8 @@ int sfa_prefill_part(int parts, const void *q, const void *k, const void *v, con
         (ring_k && (!aligned(ring_k, 16) || !aligned(ring_v, 16))) || (state && !aligned(state, 16)) ||
         !aligned(workspace, 16))
         return SFA_ERR_INVALID_ARG;
-    if (workspace_bytes < sfa::prefill_workspace_bytes(B, n, Hkv, d)) return SFA_ERR_INVALID_ARG;
+    const int Hs = s_per_query ? Hq : Hkv;
+    if (workspace_bytes < sfa::prefill_workspace_bytes(B, n, Hs, d)) return SFA_ERR_INVALID_ARG;
 
     sfa::PrefillArgs a;
     a.q = q; a.k = k; a.v = v;
@@ -79,7 +74,9 @@ int sfa_prefill_part(int parts, const void *q, const void *k, const void *v, con
     a.scale_log2e = scale_log2e(scale, d);
     a.in_bf16 = in_dtype == SFA_BF16;
     a.out_bf16 = out_dtype == SFA_BF16;
-    const size_t per = (size_t)B * Hkv * a.ntiles * d;
+    a.Hs = Hs;
+    a.s_per_query = s_per_query;
+    const size_t per = (size_t)B * Hs * a.ntiles * d;
     float *ws = static_cast<float *>(workspace);
     a.agg16 = ws;
     a.agg64 = ws + 4 * per;
@@ -87,16 +84,17 @@ int sfa_prefill_part(int parts, const void *q, const void *k, const void *v, con
     return hip_status(sfa::launch_prefill(a, static_cast<hipStream_t>(stream), parts));
 }
 
-int sfa_decode_step(const void *q, const void *k_new, const void *v_new, void *ring_k, void *ring_v,
-                    float *state, const int32_t *pos, const float *gamma, const float *alpha,
-                    void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale,
-                    int in_dtype, int out_dtype, void *stream) {
+int decode_impl(int s_per_query, const void *q, const void *k_new, const void *v_new, void *ring_k,
+                void *ring_v, float *state, const int32_t *pos, const float *gamma, const float *alpha,
+                void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale, int in_dtype,
+                int out_dtype, void *stream) {
     if (L < 0 || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return SFA_ERR_INVALID_ARG;
     if (window < 1 || window > SFA_MAX_WINDOW) return SFA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return SFA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return SFA_ERR_UNSUPPORTED;
     if (L == 0 || B == 0) return SFA_OK;
     if ((long long)L * B * Hkv >= (1LL << 31) / 64) return SFA_ERR_INVALID_ARG;  // unit indices are 32-bit
+    if ((long long)L * B * Hq >= (1LL << 31) / 128) return SFA_ERR_INVALID_ARG;  // state/query element offsets
     if (!q || !k_new || !v_new || !ring_k || !ring_v || !state || !pos || !gamma || !alpha || !out)
         return SFA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(ring_k, 16) ||
@@ -111,7 +109,53 @@ int sfa_decode_step(const void *q, const void *k_new, const void *v_new, void *r
     a.scale_log2e = scale_log2e(scale, d);
     a.in_bf16 = in_dtype == SFA_BF16;
     a.out_bf16 = out_dtype == SFA_BF16;
+    a.s_per_query = s_per_query;
     return hip_status(sfa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int sfa_prefill(const void *q, const void *k, const void *v, const float *gamma, const float *alpha,
+                void *out, void *ring_k, void *ring_v, float *state, const int32_t *pos0, int B,
+                int n, int Hq, int Hkv, int d, int window, float scale, int in_dtype, int out_dtype,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, 0, q, k, v, gamma, alpha, out, ring_k,
+                        ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype, out_dtype,
+                        workspace, workspace_bytes, stream);
+}
+
+int sfa_prefill_part(int parts, const void *q, const void *k, const void *v, const float *gamma,
+                     const float *alpha, void *out, void *ring_k, void *ring_v, float *state,
+                     const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
+                     float scale, int in_dtype, int out_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    return prefill_impl(parts, 0, q, k, v, gamma, alpha, out, ring_k, ring_v, state, pos0, B, n, Hq,
+                        Hkv, d, window, scale, in_dtype, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int sfa_prefill_qh(const void *q, const void *k, const void *v, const float *gamma, const float *alpha,
+                   void *out, void *ring_k, void *ring_v, float *state, const int32_t *pos0, int B,
+                   int n, int Hq, int Hkv, int d, int window, float scale, int in_dtype,
+                   int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, 1, q, k, v, gamma, alpha, out, ring_k,
+                        ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype, out_dtype,
+                        workspace, workspace_bytes, stream);
+}
+
+int sfa_decode_step(const void *q, const void *k_new, const void *v_new, void *ring_k, void *ring_v,
+                    float *state, const int32_t *pos, const float *gamma, const float *alpha,
+                    void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale,
+                    int in_dtype, int out_dtype, void *stream) {
+    return decode_impl(0, q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, out, L, B, Hq,
+                       Hkv, d, window, scale, in_dtype, out_dtype, stream);
+}
+
+int sfa_decode_step_qh(const void *q, const void *k_new, const void *v_new, void *ring_k,
+                       void *ring_v, float *state, const int32_t *pos, const float *gamma,
+                       const float *alpha, void *out, int L, int B, int Hq, int Hkv, int d,
+                       int window, float scale, int in_dtype, int out_dtype, void *stream) {
+    return decode_impl(1, q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, out, L, B, Hq,
+                       Hkv, d, window, scale, in_dtype, out_dtype, stream);
 }
 
 size_t sfa_enhance_workspace_size(int L, int T, int H) {

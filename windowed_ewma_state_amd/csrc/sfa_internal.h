@@ -18,6 +18,7 @@ struct DecodeArgs {
     int L, B, Hq, Hkv, d, W, group;
     float scale_log2e;
     int in_bf16, out_bf16;
+    int s_per_query;  // S and γ per query head ([L,B,Hq,d], [L,Hq]) instead of per KV head
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
@@ -35,10 +36,13 @@ struct PrefillArgs {
     int B, n, Hq, Hkv, d, W, group, ntiles;
     float scale_log2e;
     int in_bf16, out_bf16;
+    // far-field heads: Hs = Hkv (S and γ per KV head) or Hq (per query head,
+    // s_per_query = 1); the scan runs over B*Hs chains
+    int Hs, s_per_query;
     // workspace carve-up (fp32)
-    float *agg16;  // [B*Hkv][ntiles][4][d]  local EWMA aggregate of each 16-token block
-    float *agg64;  // [B*Hkv][ntiles][d]     local EWMA aggregate of each 64-token tile
-    float *carry;  // [B*Hkv][ntiles][d]     S just before each tile
+    float *agg16;  // [B*Hs][ntiles][4][d]  local EWMA aggregate of each 16-token block
+    float *agg64;  // [B*Hs][ntiles][d]     local EWMA aggregate of each 64-token tile
+    float *carry;  // [B*Hs][ntiles][d]     S just before each tile
 };
 size_t prefill_workspace_bytes(int B, int n, int Hkv, int d);
 constexpr int kPrefillScan = 1, kPrefillAttend = 2;

@@ -202,6 +202,77 @@ def decode_per_layer_graph(bufs, steps):
     return sum(a.elapsed_time(b) for a, b in ev) / steps
 
 
+def run_variants(steps=10, warmup=2):
+    """γ and the far-field state per query head (sfa_prefill_qh, sfa_decode_step_qh):
+    one 64K-token 7B-shaped prefill layer and the 28-layer decode step."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    # prefill: layer 0 of the 64K workload, one decay per query head
+    d = inputs.workload(4, device=dev, layer=0)
+    gq = inputs.uniform((HQ,), 0.90, 0.99, 77, device=dev)
+    kw = dict(window=WIN, out=torch.empty((B, N, HQ, HD), dtype=torch.bfloat16, device=dev),
+              ring_k=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
+              ring_v=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
+              state=torch.zeros((B, HQ, HD), dtype=torch.float32, device=dev),
+              workspace=torch.empty(sfa.prefill_workspace_size(B, N, HQ, HD), dtype=torch.uint8, device=dev),
+              stream=stream, gamma_per_query_head=True)
+    for _ in range(warmup):
+        sfa.prefill(d["q"], d["k"], d["v"], gq, d["alpha"], **kw)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        sfa.prefill(d["q"], d["k"], d["v"], gq, d["alpha"], **kw)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    byts = prefill_bytes_per_launch() + B * HQ * HD * 4
+    res["prefill_qh"] = {"workload": "7B-shaped 64K-token prefill layer, γ and S per query head",
+                         "us_per_call": ms * 1e3, "value": B * N * HQ / (ms * 1e-3),
+                         "unit": "tokens·heads/s",
+                         "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9,
+                                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                      "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_call": byts}}
+    del d, kw
+    torch.cuda.empty_cache()
+    # decode: the 28-layer step with S [L,B,Hq,d] and γ [L,Hq]
+    L, Bd, Hq, Hkv, hd = 28, 256, 28, 4, 128
+    sets = []
+    for i in range(3):
+        dd = inputs.decode_inputs(L, Bd, Hq, Hkv, hd, seed=4000 + i, device=dev)
+        dd["state"] = inputs.normal((L, Bd, Hq, hd), 4100 + i, 1.0, torch.float32, dev)
+        dd["gamma"] = inputs.uniform((L, Hq), 0.90, 0.99, 4200 + i, dev)
+        dd["out"] = torch.empty((L, Bd, Hq, hd), dtype=torch.bfloat16, device=dev)
+        sets.append(dd)
+
+    def call(dd):
+        sfa.decode_step(dd["q"], dd["k_new"], dd["v_new"], dd["ring_k"], dd["ring_v"], dd["state"],
+                        dd["pos"], dd["gamma"], dd["alpha"], out=dd["out"], stream=stream,
+                        gamma_per_query_head=True)
+
+    for i in range(3):
+        call(sets[i % 3])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        call(sets[i % 3])
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    byts = decode_bytes() + L * Bd * (Hq - Hkv) * hd * 4 * 2
+    res["decode_qh"] = {"workload": "7B-shaped decode step, 28 layers x 256 sequences, γ and S per query head",
+                        "us_per_step": ms * 1e3, "value": L * Bd * Hq / (ms * 1e-3),
+                        "unit": "tokens·heads/s (sequence, query head, layer)",
+                        "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9,
+                                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                     "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": byts}}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def enhance_bytes(L=24, T=4096, H=1024, S=64, R=16):
     return L * T * H * 2 * 2 + L * S * H * 4 + 2 * L * R * H * 4 + 2 * L * H * 4
 
@@ -322,7 +393,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["decode", "enhance"], default=None,
+    ap.add_argument("--only", choices=["decode", "enhance", "variants"], default=None,
                     help="run only this secondary measurement (for profiling)")
     args = ap.parse_args()
 
@@ -337,7 +408,8 @@ def main():
         copy_calibration()
         return
     if args.only:
-        print(json.dumps(run_decode() if args.only == "decode" else run_enhance()), flush=True)
+        run = {"decode": run_decode, "enhance": run_enhance, "variants": run_variants}[args.only]
+        print(json.dumps(run()), flush=True)
         return
 
     pre = run_prefill(args)
@@ -365,6 +437,7 @@ def main():
     if not args.no_secondary:
         res["decode"] = run_decode()
         res["enhance"] = run_enhance()
+        res["variants"] = run_variants()
         res["copy_ceiling_gbps"] = copy_ceiling()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.layers)

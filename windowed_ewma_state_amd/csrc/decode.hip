@@ -217,36 +217,49 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 // Each wave walks units (layer, sequence, KV head) with a stride of the grid's
 // wave count and prefetches the next unit's loads into the second of two
 // register buffers while it computes the current one.  Slots past the valid
-// ones and heads past the group read a valid row instead of being zero-filled:
-// their probabilities are exactly 0 and their outputs are never stored.  Per unit:
+// ones have masked scores and zeroed V rows; heads past the group repeat the
+// last head and their outputs are never stored.  Per unit:
 //   scores  one v_mfma_f32_16x16x32_bf16 tile per 32 head-dim elements:
-//           A = ring K rows (row = slot, the new key in slot pos mod W),
-//           B = queries (column = head); lane holds P[head l%16][slots 4(l/16)+i]
+//           A = K rows from the wave's LDS tile (row = slot, the new key in
+//           slot pos mod W), B = queries (column = head) from the same tile;
+//           lane holds P[head l%16][slots 4(l/16)+i]
 //           after the softmax, which is exactly the B operand of
 //   PV      v_mfma_f32_16x16x16_bf16 with A = V^T rows (from a per-wave LDS
 //           tile) and B = P split into bf16 hi + lo.  V^T row m of tile dt is
 //           head-dim element 32(dt/2) + 8(m/4) + 4(dt%2) + m%4, so each lane
 //           ends with 8 consecutive outputs of its head (16-byte stores).
-//   S       evicted key folded in (e-pair layout: lane owns d = 2l, 2l+1),
-//           broadcast to the epilogue through LDS.
+//   S       evicted key (read from the K tile before the new key replaces
+//           it) folded in (e-pair layout: lane owns d = 2l, 2l+1), broadcast
+//           to the epilogue through LDS.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-template <int D>
+// Every global load of a unit is row-shaped: CPR consecutive lanes read one
+// whole row (16 bytes each), so an instruction moves RPI complete rows.  On
+// this memory system whole-row requests stream markedly faster than the
+// MFMA operand shape (16 rows x 64 bytes per instruction); the operands are
+// formed from a per-wave LDS tile instead.  The ring rows are read as they
+// are (the new key/value is put into slot pos mod W in LDS), so every
+// lane's load offsets are the same for all units and only the scalar bases
+// change.
+template <int D, int QN>
 struct UnitLoads {
     static constexpr int EPL = D / kWave;
-    static constexpr int VR = D / 32;  // 16-byte V chunks per lane (4 for d 128, 2 for d 64)
-    bf16x8 kop[D / 32], qop[D / 32];
-    u32x4 v[VR];
-    float S[EPL], kev[EPL];
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int RPI = kWave / CPR;          // whole rows per load instruction (4 or 8)
+    static constexpr int NI = kMaxWindow / RPI;      // instructions per 16 rows (4 or 2)
+    // QN query instructions cover QN * RPI heads: half the register space
+    // when the group has at most 8 heads
+    u32x4 k[NI], q[QN], v[NI];
+    float S[EPL];
     uint32_t kn, vn;  // this lane's head-dim elements of k_new / v_new (raw bits)
     int p;
 };
 
-template <int D, bool QH>
-__device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoads<D> &u, int lane) {
+template <int D, int QN, bool QH>
+__device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoads<D, QN> &u, int lane) {
+    using U = UnitLoads<D, QN>;
     constexpr int EPL = D / kWave;
-    const int q4 = lane >> 4, c16 = lane & 15;
     const int G = unit % a.Hkv;
     const int lb = unit / a.Hkv;
     const int b = lb % a.B;
@@ -254,61 +267,50 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     const int p = __builtin_amdgcn_readfirstlane(a.pos[b]);
     u.p = p;
     if (p < 0) return;  // skipped unit (uniform)
-    const int s = p % W;
-    const int nvalid = (p >= W - 1) ? W : p + 1;
     const __bf16 *ringK = reinterpret_cast<const __bf16 *>(a.ring_k) + (long)unit * W * D;
     const __bf16 *ringV = reinterpret_cast<const __bf16 *>(a.ring_v) + (long)unit * W * D;
     const __bf16 *kn = reinterpret_cast<const __bf16 *>(a.k_new) + (long)unit * D;
     const __bf16 *vn = reinterpret_cast<const __bf16 *>(a.v_new) + (long)unit * D;
     const __bf16 *qg = reinterpret_cast<const __bf16 *>(a.q) + ((long)lb * a.Hq + G * group) * D;
-    // score operands: A = ring K row of slot c16 (the new key in slot pos mod W),
-    // B = query of head c16; 8 head-dim elements per lane.  Rows past the valid
-    // slots / heads are clamped to a valid row: their scores are masked and
-    // their outputs never stored, so no zero fill is needed.
-    const int krow_i = c16 < nvalid ? c16 : s;
-    const __bf16 *krow = (krow_i == s) ? kn : ringK + (long)krow_i * D;
-    const __bf16 *qrow = qg + (long)(c16 < group ? c16 : group - 1) * D;
+    const int rj = lane / U::CPR, rc = lane % U::CPR;
+    // K rows RPI*i + rj and V rows NI*rj + i (each lane then holds NI
+    // consecutive slots of V, which pair up into the dwords of the V^T tile);
+    // rows past a ring shorter than 16 repeat its last row.  Q rows = heads
+    // RPI*i + rj, as many instructions as the group needs, heads past the
+    // group repeating the last one (their outputs are never stored).
+    // (32-bit byte offsets from the unit's scalar bases)
+    constexpr uint32_t RB = D * sizeof(__bf16);
 #pragma unroll
-    for (int st = 0; st < D / 32; ++st) {
-        u.kop[st] = __builtin_bit_cast(bf16x8, ld_stream(krow + 32 * st + 8 * q4));
-        u.qop[st] = __builtin_bit_cast(bf16x8, ld_stream(qrow + 32 * st + 8 * q4));
+    for (int i = 0; i < U::NI; ++i) {
+        const uint32_t ok = (uint32_t)min(U::RPI * i + rj, W - 1) * RB + 16u * rc;
+        const uint32_t ov = (uint32_t)min(U::NI * rj + i, W - 1) * RB + 16u * rc;
+        const uint32_t oq = (uint32_t)min(U::RPI * i + rj, group - 1) * RB + 16u * rc;
+        u.k[i] = ld_stream(reinterpret_cast<const char *>(ringK) + ok);
+        u.v[i] = ld_stream(reinterpret_cast<const char *>(ringV) + ov);
+        if (i < QN) {
+            u.q[i] = u32x4{0u, 0u, 0u, 0u};
+            if (U::RPI * i < group) u.q[i] = ld_stream(reinterpret_cast<const char *>(qg) + oq);
+        }
     }
-    // V rows for the transpose: lane (m = lane % 8, c = lane / 8) holds slot rows
-    // 2m and 2m+1 at 16-byte chunks c (+ 8 for d 128); invalid slots read the new
-    // value (finite data; their probability is exactly 0)
-    const int m = lane & 7, c = lane >> 3;
-#pragma unroll
-    for (int i = 0; i < UnitLoads<D>::VR; ++i) {
-        const int r = 2 * m + (i & 1);
-        const int ch = c + 8 * (i >> 1);
-        const __bf16 *src = (r == s || r >= nvalid) ? vn : ringV + (long)r * D;
-        u.v[i] = ld_stream(src + 8 * ch);
-    }
-    // far-field state, evicted key, new key/value (e-pair layout)
+    // far-field state, new key/value (e-pair layout: lane owns d = EPL*lane ..)
     const int e0 = lane * EPL;
     if constexpr (!QH) {  // (per query head, the compute step reads its heads' S)
         const float *S_ptr = a.state + (long)unit * D + e0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) u.S[e] = S_ptr[e];
     }
-    const __bf16 *kev = ringK + (long)s * D + e0;  // position p-W when p >= W
     if (EPL == 2) {
-        const uint32_t kw = *reinterpret_cast<const uint32_t *>(kev);
-        u.kev[0] = bf16_lo(kw);
-        u.kev[EPL - 1] = bf16_hi(kw);
         u.kn = *reinterpret_cast<const uint32_t *>(kn + e0);
         u.vn = *reinterpret_cast<const uint32_t *>(vn + e0);
     } else {
-        const uint32_t kw = *reinterpret_cast<const uint16_t *>(kev);
-        u.kev[0] = bf16_bits_to_f32(kw);
         u.kn = *reinterpret_cast<const uint16_t *>(kn + e0);
         u.vn = *reinterpret_cast<const uint16_t *>(vn + e0);
     }
 }
 
-template <typename TOut, int D, bool QH>
-__device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, const UnitLoads<D> &u, int lane,
-                                             __bf16 *vt, float *sl) {
+template <typename TOut, int D, int QN, bool QH>
+__device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, const UnitLoads<D, QN> &u, int lane,
+                                             __bf16 *vt, float *sl, __bf16 *kqt) {
     constexpr int EPL = D / kWave;
     constexpr int VTS = kMaxWindow + 4;
     const int q4 = lane >> 4, c16 = lane & 15;
@@ -321,12 +323,54 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
         const int l = lb / a.B;
         const int s = p % W;
         const int nvalid = (p >= W - 1) ? W : p + 1;
-        // far field: the key of position p-W leaves the window
+        using U = UnitLoads<D, QN>;
+        constexpr int KS = D + 8;  // K/Q tile row stride (bf16): an operand read's 16 rows hit distinct banks
+        const int rj = lane / U::CPR, rc = lane % U::CPR;
+        // (a) ring K rows into the wave's tile and V into the V^T tile (row =
+        // head-dim element, 16 slots = 8 dwords per row; the lane's NI
+        // consecutive slots pair up into dword columns).  Slots past the valid
+        // ones hold whatever the ring holds: their K scores are masked, their
+        // V rows are zeroed (a probability of exactly 0 must meet finite data).
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i)
+            *reinterpret_cast<u32x4 *>(&kqt[(U::RPI * i + rj) * KS + 8 * rc]) = u.k[i];
+        u32x4 vr[U::NI];
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i) vr[i] = u.v[i];
+        if (nvalid < kMaxWindow) {
+#pragma unroll
+            for (int i = 0; i < U::NI; ++i)
+                if (U::NI * rj + i >= nvalid) vr[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int pp = 0; pp < U::NI / 2; ++pp) {
+            const int col = U::NI / 2 * rj + pp;
+            const u32x4 va = vr[2 * pp], vb = vr[2 * pp + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
+                const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
+                *reinterpret_cast<uint32_t *>(&vt[(8 * rc + 2 * i) * VTS + 2 * col]) = lo;
+                *reinterpret_cast<uint32_t *>(&vt[(8 * rc + 2 * i + 1) * VTS + 2 * col]) = hi;
+            }
+        }
+        wave_lds_sync();
+        // (b) the key of position p-W (ring slot s) leaves the window: read it
+        // from the tile before the new key takes its slot
+        const uint16_t *krow_s = reinterpret_cast<const uint16_t *>(kqt) + s * KS;
+        float kev[EPL];
+        if constexpr (EPL == 2) {
+            const uint32_t kw = *reinterpret_cast<const uint32_t *>(krow_s + e0);
+            kev[0] = bf16_lo(kw);
+            kev[EPL - 1] = bf16_hi(kw);
+        } else {
+            kev[0] = bf16_bits_to_f32(krow_s[e0]);
+        }
         float S[EPL];
         if constexpr (!QH) {
             const float gm = a.gamma[(long)l * a.Hkv + G];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * u.kev[e] : u.S[e];
+            for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * kev[e] : u.S[e];
 #pragma unroll
             for (int e = 0; e < EPL; ++e) sl[e0 + e] = S[e];
         }
@@ -338,35 +382,46 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
         float gq = 0.f;
         if constexpr (QH) {
             const float *Sg = a.state + ((long)lb * a.Hq + (long)G * group + hc) * D + 8 * q4;
-            const __bf16 *kg = reinterpret_cast<const __bf16 *>(a.ring_k) + ((long)unit * W + s) * D + 8 * q4;
 #pragma unroll
             for (int k = 0; k < D / 32; ++k)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     Sq[k][half] = *reinterpret_cast<const f32x4 *>(Sg + 32 * k + 4 * half);
-                    kq[k][half] = *reinterpret_cast<const u32x2 *>(kg + 32 * k + 4 * half);
+                    kq[k][half] = *reinterpret_cast<const u32x2 *>(krow_s + 32 * k + 8 * q4 + 4 * half);
                 }
             gq = a.gamma[(long)l * a.Hq + (long)G * group + hc];
         }
-        // V^T tile: row = head-dim element, 16 slots per row; consecutive
-        // lanes write consecutive dwords (slot pairs)
-        const int m = lane & 7, c = lane >> 3;
-#pragma unroll
-        for (int pr = 0; pr < UnitLoads<D>::VR / 2; ++pr) {
-            const int ch = c + 8 * pr;
-            const u32x4 va = u.v[2 * pr], vb = u.v[2 * pr + 1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
-                const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
-                *reinterpret_cast<uint32_t *>(&vt[(8 * ch + 2 * i) * VTS + 2 * m]) = lo;
-                *reinterpret_cast<uint32_t *>(&vt[(8 * ch + 2 * i + 1) * VTS + 2 * m]) = hi;
-            }
+        wave_lds_sync();
+        // (c) the new key and value into slot s
+        if constexpr (EPL == 2) {
+            *reinterpret_cast<uint32_t *>(&kqt[s * KS + e0]) = u.kn;
+            reinterpret_cast<uint16_t *>(vt)[e0 * VTS + s] = (uint16_t)(u.vn & 0xffffu);
+            reinterpret_cast<uint16_t *>(vt)[(e0 + 1) * VTS + s] = (uint16_t)(u.vn >> 16);
+        } else {
+            reinterpret_cast<uint16_t *>(kqt)[s * KS + e0] = (uint16_t)u.kn;
+            reinterpret_cast<uint16_t *>(vt)[e0 * VTS + s] = (uint16_t)u.vn;
         }
+        wave_lds_sync();
+        // (d) A operands (row = slot c16, 8 head-dim elements at 32 st + 8 q4),
+        // then the same tile takes the queries (row = head = B operand column)
+        bf16x8 kop[D / 32], qop[D / 32];
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st)
+            kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&kqt[c16 * KS + 32 * st + 8 * q4]));
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < QN; ++i)
+            if (U::RPI * i < group)
+                *reinterpret_cast<u32x4 *>(&kqt[(U::RPI * i + rj) * KS + 8 * rc]) = u.q[i];
+        wave_lds_sync();
+        const int hr = c16 < group ? c16 : group - 1;
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st)
+            qop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&kqt[hr * KS + 32 * st + 8 * q4]));
         // scores and softmax over the valid slots
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < D / 32; ++st) sc = mfma_bf16_16x16x32(u.kop[st], u.qop[st], sc);
+        for (int st = 0; st < D / 32; ++st) sc = mfma_bf16_16x16x32(kop[st], qop[st], sc);
         float x[4], mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -465,11 +520,12 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
     }
 }
 
-template <typename TOut, int D, bool QH>
+template <typename TOut, int D, int QN, bool QH>
 __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
     constexpr int VTS = kMaxWindow + 4;  // V^T row stride (bf16): 16 slots + pad
     __shared__ __attribute__((aligned(16))) __bf16 Vt[4][D * VTS];
     __shared__ __attribute__((aligned(16))) float Sl[4][D];
+    __shared__ __attribute__((aligned(16))) __bf16 KQ[4][kMaxWindow * (D + 8)];  // K, then Q rows
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -478,25 +534,28 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
     int unit = blockIdx.x * 4 + wave;
     __bf16 *vt = Vt[wave];
     float *sl = Sl[wave];
+    __bf16 *kqt = KQ[wave];
 
     // two register buffers in turn: the next unit's loads are in flight while
     // the current one computes
-    UnitLoads<D> A, Bf;
-    if (unit < n_units) unit_load<D, QH>(a, unit, A, lane);
+    UnitLoads<D, QN> A, Bf;
+    if (unit < n_units) unit_load<D, QN, QH>(a, unit, A, lane);
     while (unit < n_units) {
-        if (unit + stride < n_units) unit_load<D, QH>(a, unit + stride, Bf, lane);
-        unit_compute<TOut, D, QH>(a, unit, A, lane, vt, sl);
+        if (unit + stride < n_units) unit_load<D, QN, QH>(a, unit + stride, Bf, lane);
+        unit_compute<TOut, D, QN, QH>(a, unit, A, lane, vt, sl, kqt);
         unit += stride;
         if (unit >= n_units) break;
-        if (unit + stride < n_units) unit_load<D, QH>(a, unit + stride, A, lane);
-        unit_compute<TOut, D, QH>(a, unit, Bf, lane, vt, sl);
+        if (unit + stride < n_units) unit_load<D, QN, QH>(a, unit + stride, A, lane);
+        unit_compute<TOut, D, QN, QH>(a, unit, Bf, lane, vt, sl, kqt);
         unit += stride;
     }
 }
 
 // Grid of one wave per (unit, unit + stride, ...) chain: no more blocks than the
-// device holds at once (one round of waves, no partly filled tail round), and
-// at least two units per wave so that every wave overlaps a prefetch with compute.
+// device holds at once (one round of waves, no partly filled tail round) and no
+// more waves than units.  A launch smaller than the resident capacity (one
+// layer, say) runs one unit per wave: more units in flight beat the prefetch
+// overlap that several units per wave would give.
 template <typename K>
 hipError_t launch_persistent(K kernel, const DecodeArgs &a, long units, hipStream_t stream) {
     static std::atomic<int> resident[kMaxDevices];
@@ -514,7 +573,7 @@ hipError_t launch_persistent(K kernel, const DecodeArgs &a, long units, hipStrea
         cap = std::max(1, cus * std::max(1, per_cu));
         resident[dev].store(cap, std::memory_order_relaxed);
     }
-    const long blocks = std::max<long>(1, std::min<long>(cap, (units + 7) / 8));
+    const long blocks = std::max<long>(1, std::min<long>(cap, (units + 3) / 4));
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
@@ -524,8 +583,13 @@ hipError_t launch_q(const DecodeArgs &a, hipStream_t stream) {
     const long units = (long)a.L * a.B * a.Hkv;
     if constexpr (std::is_same<TIn, __bf16>::value) {
         if (a.group <= 16) {
-            if (a.d == 128) return launch_persistent(k_decode_mfma<TOut, 128, QH>, a, units, stream);
-            return launch_persistent(k_decode_mfma<TOut, 64, QH>, a, units, stream);
+            // query rows per load instruction: 4 (d 128) or 8 (d 64)
+            const bool half = a.group <= 8;
+            if (a.d == 128)
+                return half ? launch_persistent(k_decode_mfma<TOut, 128, 2, QH>, a, units, stream)
+                            : launch_persistent(k_decode_mfma<TOut, 128, 4, QH>, a, units, stream);
+            return half ? launch_persistent(k_decode_mfma<TOut, 64, 1, QH>, a, units, stream)
+                        : launch_persistent(k_decode_mfma<TOut, 64, 2, QH>, a, units, stream);
         }
     }
     const dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock));

@@ -51,6 +51,14 @@ __device__ __forceinline__ float sum_over_groups(float x) {
     return x;
 }
 
+// orders a wave's LDS writes before its later LDS reads (and reads before
+// later overwrites) of a tile no other wave touches
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---- typed element access -------------------------------------------------
 template <typename T> struct Elem;
 template <> struct Elem<float> {

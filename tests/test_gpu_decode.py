@@ -105,3 +105,40 @@ def test_decode_steps_continue_a_gpu_prefill():
     check_exact(rk[0], frk, "ring_k")
     check_exact(rv[0], frv, "ring_v")
     check_state(st[0], fst)
+
+
+def _skip_case(d, skip, qh):
+    """Run with pos[skip] = -1; check the skipped sequence is untouched (bit for
+    bit) and the others match the oracle run on the batch without it."""
+    keep = [b for b in range(d["pos"].numel()) if b != skip]
+    pos = d["pos"].clone()
+    pos[skip] = -1
+    sentinel = torch.full(d["q"].shape, 7.25, dtype=torch.float32)
+    out = sentinel.cuda()
+    rk, rv, st = d["ring_k"].cuda(), d["ring_v"].cuda(), d["state"].cuda()
+    sfa.decode_step(d["q"].cuda(), d["k_new"].cuda(), d["v_new"].cuda(), rk, rv, st, pos.cuda(),
+                    d["gamma"].cuda(), d["alpha"].cuda(), out=out, gamma_per_query_head=qh)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, skip].cpu(), sentinel[:, skip]), "skipped sequence: out written"
+    assert torch.equal(rk[:, skip].cpu(), d["ring_k"][:, skip]), "skipped sequence: ring_k written"
+    assert torch.equal(rv[:, skip].cpu(), d["ring_v"][:, skip]), "skipped sequence: ring_v written"
+    assert torch.equal(st[:, skip].cpu(), d["state"][:, skip]), "skipped sequence: state written"
+    sub = {k_: (v_[:, keep].contiguous() if k_ not in ("gamma", "alpha", "pos", "window") else v_)
+           for k_, v_ in d.items()}
+    sub["pos"] = d["pos"][keep].contiguous()
+    ref = oracle.decode_step(sub["q"], sub["k_new"], sub["v_new"], sub["ring_k"], sub["ring_v"],
+                             sub["state"], sub["pos"], sub["gamma"], sub["alpha"], s_per_query=qh)
+    check_output(out[:, keep], ref[0], d["q"].dtype == torch.bfloat16, "out (kept sequences)")
+    check_exact(rk[:, keep], ref[1], "ring_k")
+    check_exact(rv[:, keep], ref[2], "ring_v")
+    check_state(st[:, keep], ref[3])
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_decode_negative_position_skips_the_sequence(hd):
+    """A negative pos entry leaves that sequence's out, ring and S untouched."""
+    L, B, Hq, Hkv = 3, 6, 8, 2
+    log(f"decode skip case hd {hd}")
+    d = inputs.decode_inputs(L, B, Hq, Hkv, hd, seed=31 + hd)
+    d["pos"] = torch.tensor([3, 40, 16, 15, 200, 7], dtype=torch.int32)
+    _skip_case(d, 2, False)

@@ -147,3 +147,15 @@ def test_decode_qh_continues_a_gpu_prefill_qh():
     torch.cuda.synchronize()
     check_output(torch.stack(outs, 1), ref[0][:, n:], True, "decode out")
     check_state(st, ref[3])
+
+
+def test_decode_qh_negative_position_skips_the_sequence():
+    """Per query head: a negative pos entry leaves that sequence untouched."""
+    from tests.test_gpu_decode import _skip_case
+    L, B, Hq, Hkv, hd = 2, 5, 14, 2, 128
+    log("decode_qh skip case")
+    d = inputs.decode_inputs(L, B, Hq, Hkv, hd, seed=41)
+    d["state"] = inputs.normal((L, B, Hq, hd), 4242, 1.0, torch.float32)
+    d["gamma"] = inputs.uniform((L, Hq), 0.90, 0.99, 4343)
+    d["pos"] = torch.tensor([5, 100, 16, 3, 31], dtype=torch.int32)
+    _skip_case(d, 1, True)

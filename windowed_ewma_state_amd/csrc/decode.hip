@@ -253,20 +253,32 @@ struct UnitLoads {
     u32x4 k[NI], q[QN], v[NI];
     float S[EPL];
     uint32_t kn, vn;  // this lane's head-dim elements of k_new / v_new (raw bits)
-    int p;
+    float gm;         // γ of the unit's S (per query head: of head c16)
+    float al;         // α of head c16 (0 past the group)
+    int p;            // the sequence's position
 };
 
+// `live` false: the loop's last prefetch, issued anyway (see k_decode_mfma)
+// with every lane of an instruction at one 16-byte chunk of the unit.
 template <int D, int QN, bool QH>
-__device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoads<D, QN> &u, int lane) {
+__device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoads<D, QN> &u, int lane, bool live) {
     using U = UnitLoads<D, QN>;
     constexpr int EPL = D / kWave;
     const int G = unit % a.Hkv;
     const int lb = unit / a.Hkv;
     const int b = lb % a.B;
     const int W = a.W, group = a.group;
-    const int p = __builtin_amdgcn_readfirstlane(a.pos[b]);
-    u.p = p;
-    if (p < 0) return;  // skipped unit (uniform)
+    // No load here depends on the position, and every small value the step
+    // needs (position, γ, α) is loaded with the unit: the counter of
+    // outstanding loads drains in issue order, so a load issued during the
+    // previous unit's compute would make that compute wait for this whole
+    // prefetch.
+    u.p = load_uniform(a.pos + b);
+    const int l = lb / a.B;
+    const int c16 = lane & 15;
+    const int hc = live && c16 < group ? c16 : group - 1;
+    u.gm = QH ? a.gamma[(long)l * a.Hq + (long)G * group + hc] : load_uniform(a.gamma + (long)l * a.Hkv + G);
+    u.al = a.alpha[(long)l * a.Hq + (long)G * group + hc];
     const __bf16 *ringK = reinterpret_cast<const __bf16 *>(a.ring_k) + (long)unit * W * D;
     const __bf16 *ringV = reinterpret_cast<const __bf16 *>(a.ring_v) + (long)unit * W * D;
     const __bf16 *kn = reinterpret_cast<const __bf16 *>(a.k_new) + (long)unit * D;
@@ -277,23 +289,23 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     // consecutive slots of V, which pair up into the dwords of the V^T tile);
     // rows past a ring shorter than 16 repeat its last row.  Q rows = heads
     // RPI*i + rj, as many instructions as the group needs, heads past the
-    // group repeating the last one (their outputs are never stored).
-    // (32-bit byte offsets from the unit's scalar bases)
+    // group repeating the last one (the step computes and stores that head's
+    // output for them once more, bit for bit the same).  Every load is
+    // issued, whatever the group size, so the number of loads in flight is a
+    // compile-time constant.  (32-bit byte offsets from the unit's scalar bases)
     constexpr uint32_t RB = D * sizeof(__bf16);
+    const uint32_t lm = live ? ~0u : 0u;
 #pragma unroll
     for (int i = 0; i < U::NI; ++i) {
-        const uint32_t ok = (uint32_t)min(U::RPI * i + rj, W - 1) * RB + 16u * rc;
-        const uint32_t ov = (uint32_t)min(U::NI * rj + i, W - 1) * RB + 16u * rc;
-        const uint32_t oq = (uint32_t)min(U::RPI * i + rj, group - 1) * RB + 16u * rc;
+        const uint32_t ok = ((uint32_t)min(U::RPI * i + rj, W - 1) * RB + 16u * rc) & lm;
+        const uint32_t ov = ((uint32_t)min(U::NI * rj + i, W - 1) * RB + 16u * rc) & lm;
+        const uint32_t oq = ((uint32_t)min(U::RPI * i + rj, group - 1) * RB + 16u * rc) & lm;
         u.k[i] = ld_stream(reinterpret_cast<const char *>(ringK) + ok);
         u.v[i] = ld_stream(reinterpret_cast<const char *>(ringV) + ov);
-        if (i < QN) {
-            u.q[i] = u32x4{0u, 0u, 0u, 0u};
-            if (U::RPI * i < group) u.q[i] = ld_stream(reinterpret_cast<const char *>(qg) + oq);
-        }
+        if (i < QN) u.q[i] = ld_stream(reinterpret_cast<const char *>(qg) + oq);
     }
     // far-field state, new key/value (e-pair layout: lane owns d = EPL*lane ..)
-    const int e0 = lane * EPL;
+    const int e0 = live ? lane * EPL : 0;
     if constexpr (!QH) {  // (per query head, the compute step reads its heads' S)
         const float *S_ptr = a.state + (long)unit * D + e0;
 #pragma unroll
@@ -308,19 +320,51 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     }
 }
 
+// Per query head, the S rows of the unit's heads in the epilogue layout (lane
+// (q4, c16): head c16 at d = 32k + 8q4 + 4half + i), loaded just before the
+// next unit's prefetch.
+template <int D, bool QH> struct LateLoads { f32x4 Sq[QH ? D / 32 : 1][2]; };
+
+template <int D, bool QH>
+__device__ __forceinline__ void late_load(const DecodeArgs &a, int unit, LateLoads<D, QH> &L, int lane) {
+    if constexpr (QH) {
+        const int q4 = lane >> 4, c16 = lane & 15;
+        const int G = unit % a.Hkv, lb = unit / a.Hkv;
+        const int hc = c16 < a.group ? c16 : a.group - 1;
+        const float *Sg = a.state + ((long)lb * a.Hq + (long)G * a.group + hc) * D + 8 * q4;
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                L.Sq[k][half] = *reinterpret_cast<const f32x4 *>(Sg + 32 * k + 4 * half);
+    }
+}
+
+// Target of the stores of a unit whose position is negative (it must be left
+// untouched): the store is issued all the same, 16 bytes per lane.
+__device__ __attribute__((aligned(256))) uint32_t g_decode_sink[kWave * 4];
+
+template <typename T>
+__device__ __forceinline__ T *sink_or(T *p, bool skip, int lane) {
+    return skip ? reinterpret_cast<T *>(g_decode_sink + 4 * lane) : p;
+}
+
 template <typename TOut, int D, int QN, bool QH>
-__device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, const UnitLoads<D, QN> &u, int lane,
-                                             __bf16 *vt, float *sl, __bf16 *kqt) {
+__device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, const UnitLoads<D, QN> &u,
+                                             const LateLoads<D, QH> &late, int lane, __bf16 *vt, float *sl,
+                                             __bf16 *kqt) {
     constexpr int EPL = D / kWave;
     constexpr int VTS = kMaxWindow + 4;
     const int q4 = lane >> 4, c16 = lane & 15;
     const int W = a.W, group = a.group;
     const int e0 = lane * EPL;
-    const int p = u.p;
-    if (p >= 0) {
+    // A negative position leaves the unit untouched: the step runs as for
+    // position 0 and every store of it goes to the sink.
+    const bool skip = u.p < 0;
+    const int p = skip ? 0 : u.p;
+    {
         const int G = unit % a.Hkv;
         const int lb = unit / a.Hkv;
-        const int l = lb / a.B;
         const int s = p % W;
         const int nvalid = (p >= W - 1) ? W : p + 1;
         using U = UnitLoads<D, QN>;
@@ -368,7 +412,7 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
         }
         float S[EPL];
         if constexpr (!QH) {
-            const float gm = a.gamma[(long)l * a.Hkv + G];
+            const float gm = u.gm;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * kev[e] : u.S[e];
 #pragma unroll
@@ -381,15 +425,14 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
         u32x2 kq[QH ? D / 32 : 1][2];
         float gq = 0.f;
         if constexpr (QH) {
-            const float *Sg = a.state + ((long)lb * a.Hq + (long)G * group + hc) * D + 8 * q4;
 #pragma unroll
             for (int k = 0; k < D / 32; ++k)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    Sq[k][half] = *reinterpret_cast<const f32x4 *>(Sg + 32 * k + 4 * half);
+                    Sq[k][half] = late.Sq[k][half];
                     kq[k][half] = *reinterpret_cast<const u32x2 *>(krow_s + 32 * k + 8 * q4 + 4 * half);
                 }
-            gq = a.gamma[(long)l * a.Hq + (long)G * group + hc];
+            gq = u.gm;
         }
         wave_lds_sync();
         // (c) the new key and value into slot s
@@ -448,9 +491,8 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        const bool head_ok = c16 < group;
-        const float al = head_ok ? a.alpha[(long)l * a.Hq + (long)G * group + c16] : 0.f;
-        TOut *orow = reinterpret_cast<TOut *>(a.out) + ((long)lb * a.Hq + G * group + c16) * D;
+        const float al = u.al;
+        TOut *orow = reinterpret_cast<TOut *>(a.out) + ((long)lb * a.Hq + G * group + hc) * D;
 #pragma unroll
         for (int k = 0; k < D / 32; ++k) {
             float ov[8];
@@ -477,38 +519,34 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ov[4 * half + i] = fmaf(al, s4[i], o[i]);
             }
-            if (head_ok) {
-                if constexpr (std::is_same<TOut, float>::value) {
-                    *reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-                    *reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4 + 4) = make_float4(ov[4], ov[5], ov[6], ov[7]);
-                } else {
-                    u32x4 w;
+            if constexpr (std::is_same<TOut, float>::value) {
+                *sink_or(reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4), skip, lane) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+                *sink_or(reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4 + 4), skip, lane) = make_float4(ov[4], ov[5], ov[6], ov[7]);
+            } else {
+                u32x4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
-                    st_stream(orow + 32 * k + 8 * q4, w);
-                }
+                for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
+                st_stream(sink_or(reinterpret_cast<u32x4 *>(orow + 32 * k + 8 * q4), skip, lane), w);
             }
         }
         // cache update (every read of this unit's ring is done)
         if constexpr (QH) {
-            if (head_ok) {
-                float *Sg = a.state + ((long)lb * a.Hq + (long)G * group + c16) * D + 8 * q4;
+            float *Sg = a.state + ((long)lb * a.Hq + (long)G * group + hc) * D + 8 * q4;
 #pragma unroll
-                for (int k = 0; k < D / 32; ++k)
+            for (int k = 0; k < D / 32; ++k)
 #pragma unroll
-                    for (int half = 0; half < 2; ++half)
-                        *reinterpret_cast<f32x4 *>(Sg + 32 * k + 4 * half) = Sq[k][half];
-            }
+                for (int half = 0; half < 2; ++half)
+                    *sink_or(reinterpret_cast<f32x4 *>(Sg + 32 * k + 4 * half), skip, lane) = Sq[k][half];
         } else {
             float *S_ptr = a.state + (long)unit * D + e0;
             if constexpr (EPL == 2) {
-                *reinterpret_cast<float2 *>(S_ptr) = make_float2(S[0], S[EPL - 1]);
+                *sink_or(reinterpret_cast<float2 *>(S_ptr), skip, lane) = make_float2(S[0], S[EPL - 1]);
             } else {
-                S_ptr[0] = S[0];
+                *sink_or(S_ptr, skip, lane) = S[0];
             }
         }
-        __bf16 *ringK = reinterpret_cast<__bf16 *>(a.ring_k) + ((long)unit * W + s) * D + e0;
-        __bf16 *ringV = reinterpret_cast<__bf16 *>(a.ring_v) + ((long)unit * W + s) * D + e0;
+        __bf16 *ringK = sink_or(reinterpret_cast<__bf16 *>(a.ring_k) + ((long)unit * W + s) * D + e0, skip, lane);
+        __bf16 *ringV = sink_or(reinterpret_cast<__bf16 *>(a.ring_v) + ((long)unit * W + s) * D + e0, skip, lane);
         if constexpr (EPL == 2) {
             *reinterpret_cast<uint32_t *>(ringK) = u.kn;
             *reinterpret_cast<uint32_t *>(ringV) = u.vn;
@@ -536,18 +574,37 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
     float *sl = Sl[wave];
     __bf16 *kqt = KQ[wave];
 
-    // two register buffers in turn: the next unit's loads are in flight while
-    // the current one computes
+    // Two register buffers in turn: the next unit's loads are in flight while
+    // the current one computes.  The count of outstanding memory operations
+    // drains in issue order and the compiler waits on it by position, so every
+    // path issues the same loads and stores: the last prefetch is issued too
+    // (all lanes at one chunk), the per-query-head S rows of a unit go out
+    // before the next unit's prefetch, no store is skipped, and the first step
+    // is peeled so that the loop is entered with the same history as its back
+    // edge (the previous step's stores after the prefetch).
+    if (unit >= n_units) return;
     UnitLoads<D, QN> A, Bf;
-    if (unit < n_units) unit_load<D, QN, QH>(a, unit, A, lane);
-    while (unit < n_units) {
-        if (unit + stride < n_units) unit_load<D, QN, QH>(a, unit + stride, Bf, lane);
-        unit_compute<TOut, D, QN, QH>(a, unit, A, lane, vt, sl, kqt);
-        unit += stride;
-        if (unit >= n_units) break;
-        if (unit + stride < n_units) unit_load<D, QN, QH>(a, unit + stride, A, lane);
-        unit_compute<TOut, D, QN, QH>(a, unit, Bf, lane, vt, sl, kqt);
-        unit += stride;
+    LateLoads<D, QH> late;
+    unit_load<D, QN, QH>(a, unit, A, lane, true);
+    int next = unit + stride;
+    bool more = next < n_units;
+    late_load<D, QH>(a, unit, late, lane);
+    unit_load<D, QN, QH>(a, more ? next : unit, Bf, lane, more);
+    unit_compute<TOut, D, QN, QH>(a, unit, A, late, lane, vt, sl, kqt);
+    while (more) {
+        unit = next;
+        next = unit + stride;
+        more = next < n_units;
+        late_load<D, QH>(a, unit, late, lane);
+        unit_load<D, QN, QH>(a, more ? next : unit, A, lane, more);
+        unit_compute<TOut, D, QN, QH>(a, unit, Bf, late, lane, vt, sl, kqt);
+        if (!more) break;
+        unit = next;
+        next = unit + stride;
+        more = next < n_units;
+        late_load<D, QH>(a, unit, late, lane);
+        unit_load<D, QN, QH>(a, more ? next : unit, Bf, lane, more);
+        unit_compute<TOut, D, QN, QH>(a, unit, A, late, lane, vt, sl, kqt);
     }
 }
 

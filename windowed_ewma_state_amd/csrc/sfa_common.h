@@ -59,6 +59,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Load of a wave-uniform value through the scalar data cache (s_load): the
+// address must be the same in every lane and the data must not be written
+// while the kernel runs.  Scalar loads are counted apart from vector memory
+// loads, so waiting for one never waits for vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
 // ---- typed element access -------------------------------------------------
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -353,11 +353,13 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
         const float *C = a.carry + tbase * D + e0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) Cx[e] = C[e];
+        // (all three blocks are loaded unconditionally, in bounds for every
+        // wave; only w < wave are used)
 #pragma unroll
         for (int w = 0; w < 3; ++w) {
             const float *A = a.agg16 + (tbase * 4 + w) * D + e0;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) Ax[w][e] = w < wave ? A[e] : 0.f;
+            for (int e = 0; e < EPL; ++e) Ax[w][e] = A[e];
         }
     };
     // QH: chain of query head h of this group
@@ -366,55 +368,112 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     carry_loads(chain0, Cin, Ain);
 
     // ---- (1) stage K rows (row-major) and V (transposed) ---------------------
-    for (int idx = tid; idx < kRows * CPR; idx += 256) {
-        const int r = idx / CPR, c = idx % CPR;
-        const int t = t0 - kMaxWindow + r;
-        const TIn *src = kv_row(Kbg, row_stride, ringKr, t, n, p0, W, D);
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (src) val = *reinterpret_cast<const u32x4 *>(src + c * EPC);
-        *reinterpret_cast<u32x4 *>(&Klds[r * KS + c * EPC]) = val;
-        if (write_ring && t >= t0 && t < n && t >= n - W)
-            *reinterpret_cast<u32x4 *>(ringKw + (long)(t % W) * D + c * EPC) = val;
+    // Every load of the staging is issued before the first LDS write, so the
+    // tile waits for one memory latency, not one per chunk.
+    constexpr int KCH = kRows * CPR;  // 16-byte chunks of the staged K rows
+    constexpr int KIT = (KCH + 255) / 256;
+    u32x4 kst[KIT];
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+        const int idx = tid + 256 * it;
+        kst[it] = u32x4{0u, 0u, 0u, 0u};
+        if (idx < KCH) {
+            const TIn *src = kv_row(Kbg, row_stride, ringKr, t0 - kMaxWindow + idx / CPR, n, p0, W, D);
+            if (src) kst[it] = *reinterpret_cast<const u32x4 *>(src + (idx % CPR) * EPC);
+        }
     }
     if constexpr (kBf16) {
         // two keys per thread so each LDS write is one aligned dword; key pairs
         // vary fastest across lanes so a write instruction hits consecutive banks
         constexpr int kPairs = kRows / 2;
-        for (int idx = tid; idx < kPairs * CPR; idx += 256) {
-            const int m = idx % kPairs, c = idx / kPairs;
-            const int ta = t0 - kMaxWindow + 2 * m;
-            const TIn *sa = kv_row(Vbg, row_stride, ringVr, ta, n, p0, W, D);
-            const TIn *sb = kv_row(Vbg, row_stride, ringVr, ta + 1, n, p0, W, D);
-            u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-            if (sa) va = *reinterpret_cast<const u32x4 *>(sa + c * EPC);
-            if (sb) vb = *reinterpret_cast<const u32x4 *>(sb + c * EPC);
+        constexpr int VCH = kPairs * CPR;
+        constexpr int VIT = (VCH + 255) / 256;
+        u32x4 vsa[VIT], vsb[VIT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
-                const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
-                reinterpret_cast<uint32_t *>(Vt)[vt_dword(c * EPC + 2 * i, m)] = lo;
-                reinterpret_cast<uint32_t *>(Vt)[vt_dword(c * EPC + 2 * i + 1, m)] = hi;
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = tid + 256 * it;
+            vsa[it] = vsb[it] = u32x4{0u, 0u, 0u, 0u};
+            if (idx < VCH) {
+                const int m = idx % kPairs, c = idx / kPairs;
+                const int ta = t0 - kMaxWindow + 2 * m;
+                const TIn *sa = kv_row(Vbg, row_stride, ringVr, ta, n, p0, W, D);
+                const TIn *sb = kv_row(Vbg, row_stride, ringVr, ta + 1, n, p0, W, D);
+                if (sa) vsa[it] = *reinterpret_cast<const u32x4 *>(sa + c * EPC);
+                if (sb) vsb[it] = *reinterpret_cast<const u32x4 *>(sb + c * EPC);
             }
-            if (write_ring) {
-                if (ta >= t0 && ta < n && ta >= n - W)
-                    *reinterpret_cast<u32x4 *>(ringVw + (long)(ta % W) * D + c * EPC) = va;
-                if (ta + 1 >= t0 && ta + 1 < n && ta + 1 >= n - W)
-                    *reinterpret_cast<u32x4 *>(ringVw + (long)((ta + 1) % W) * D + c * EPC) = vb;
+        }
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+            const int idx = tid + 256 * it;
+            if (idx < KCH) {
+                const int r = idx / CPR, c = idx % CPR;
+                const int t = t0 - kMaxWindow + r;
+                *reinterpret_cast<u32x4 *>(&Klds[r * KS + c * EPC]) = kst[it];
+                if (write_ring && t >= t0 && t < n && t >= n - W)
+                    *reinterpret_cast<u32x4 *>(ringKw + (long)(t % W) * D + c * EPC) = kst[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = tid + 256 * it;
+            if (idx < VCH) {
+                const int m = idx % kPairs, c = idx / kPairs;
+                const int ta = t0 - kMaxWindow + 2 * m;
+                const u32x4 va = vsa[it], vb = vsb[it];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = (va[i] & 0xffffu) | (vb[i] << 16);
+                    const uint32_t hi = (va[i] >> 16) | (vb[i] & 0xffff0000u);
+                    reinterpret_cast<uint32_t *>(Vt)[vt_dword(c * EPC + 2 * i, m)] = lo;
+                    reinterpret_cast<uint32_t *>(Vt)[vt_dword(c * EPC + 2 * i + 1, m)] = hi;
+                }
+                if (write_ring) {
+                    if (ta >= t0 && ta < n && ta >= n - W)
+                        *reinterpret_cast<u32x4 *>(ringVw + (long)(ta % W) * D + c * EPC) = va;
+                    if (ta + 1 >= t0 && ta + 1 < n && ta + 1 >= n - W)
+                        *reinterpret_cast<u32x4 *>(ringVw + (long)((ta + 1) % W) * D + c * EPC) = vb;
+                }
             }
         }
     } else {
-        for (int idx = tid; idx < kRows * CPR; idx += 256) {
-            const int r = idx % kRows, c = idx / kRows;
-            const int t = t0 - kMaxWindow + r;
-            const TIn *src = kv_row(Vbg, row_stride, ringVr, t, n, p0, W, D);
-            float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (src) val = *reinterpret_cast<const float4 *>(src + c * EPC);
-            Vt[(c * EPC + 0) * VS + r] = val.x;
-            Vt[(c * EPC + 1) * VS + r] = val.y;
-            Vt[(c * EPC + 2) * VS + r] = val.z;
-            Vt[(c * EPC + 3) * VS + r] = val.w;
-            if (write_ring && t >= t0 && t < n && t >= n - W)
-                *reinterpret_cast<float4 *>(ringVw + (long)(t % W) * D + c * EPC) = val;
+        constexpr int VCH = kRows * CPR;
+        constexpr int VIT = (VCH + 255) / 256;
+        float4 vs[VIT];
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = tid + 256 * it;
+            vs[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (idx < VCH) {
+                const int r = idx % kRows, c = idx / kRows;
+                const TIn *src = kv_row(Vbg, row_stride, ringVr, t0 - kMaxWindow + r, n, p0, W, D);
+                if (src) vs[it] = *reinterpret_cast<const float4 *>(src + c * EPC);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+            const int idx = tid + 256 * it;
+            if (idx < KCH) {
+                const int r = idx / CPR, c = idx % CPR;
+                const int t = t0 - kMaxWindow + r;
+                *reinterpret_cast<u32x4 *>(&Klds[r * KS + c * EPC]) = kst[it];
+                if (write_ring && t >= t0 && t < n && t >= n - W)
+                    *reinterpret_cast<u32x4 *>(ringKw + (long)(t % W) * D + c * EPC) = kst[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = tid + 256 * it;
+            if (idx < VCH) {
+                const int r = idx % kRows, c = idx / kRows;
+                const int t = t0 - kMaxWindow + r;
+                const float4 val = vs[it];
+                Vt[(c * EPC + 0) * VS + r] = val.x;
+                Vt[(c * EPC + 1) * VS + r] = val.y;
+                Vt[(c * EPC + 2) * VS + r] = val.z;
+                Vt[(c * EPC + 3) * VS + r] = val.w;
+                if (write_ring && t >= t0 && t < n && t >= n - W)
+                    *reinterpret_cast<float4 *>(ringVw + (long)(t % W) * D + c * EPC) = val;
+            }
         }
     }
 
@@ -468,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // head's carry loads go out here
     auto head_S = [&](int h) {
         if constexpr (QH) {
-            const float gh = a.gamma[chain0 - (long)b * a.Hq + h];
+            const float gh = load_uniform(a.gamma + (chain0 - (long)b * a.Hq + h));
             float Cx[EPL], Ax[3][EPL], S[EPL];
 #pragma unroll
             for (int e = 0; e < EPL; ++e) Cx[e] = Cin[e];
@@ -581,7 +640,9 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
                     Ph[i] = hi_;
                     Pl[i] = lo_;
                 }
-                const float al = alpha[h];
+                // (a scalar load: a vector load here would make the wait for it
+                // also wait for the query prefetch issued just before)
+                const float al = load_uniform(alpha + h);
                 // PV in 16-row V^T tiles; row m of tile dt is head-dim element
                 // 32(dt/2) + 8(m/4) + 4(dt%2) + m%4, so after tiles 2k and 2k+1
                 // lane group q4 holds elements [32k + 8q4, +8) of its token and
@@ -672,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             const float inv = 1.f / sum;
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] *= inv;
-            const float al = alpha[hh];
+            const float al = load_uniform(alpha + hh);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
                 // k-step s: lane group q4 supplies key 4*q4 + s of tile s/4

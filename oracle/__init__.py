@@ -54,9 +54,9 @@ def _load():
         P = ctypes.c_void_p
         I = ctypes.c_int
         D = ctypes.c_double
-        lib.oracle_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I]
+        lib.oracle_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I]
         lib.oracle_prefill.restype = None
-        lib.oracle_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I]
+        lib.oracle_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I]
         lib.oracle_decode_step.restype = None
         lib.oracle_enhance.argtypes = [P, P, P, P, P, ctypes.c_long, P,
                                        I, I, I, I, I, I, D, D, D, D, D, I, I]
@@ -95,13 +95,16 @@ def alpha_layer(alpha_base: float, cross_decay: float, layer: int, n_layers: int
 
 
 def prefill(q, k, v, gamma, alpha, window: int, scale: float = 0.0,
-            ring_k=None, ring_v=None, state=None, pos0=None, s_per_query: bool = False):
+            ring_k=None, ring_v=None, state=None, pos0=None, s_per_query: bool = False,
+            running_mean: bool = False):
     """Windowed softmax attention plus EWMA far field over one prompt ([P1] 2.1).
 
     q [B,n,Hq,d]; k, v [B,n,Hkv,d]; gamma [Hkv]; alpha [Hq].
     Optional continuation: ring_k/ring_v [B,Hkv,W,d], state [B,Hkv,d] and
     pos0 [B] (positions of the first token); absent means a fresh sequence.
     s_per_query: γ [Hq] and S [B,Hq,d] per query head instead of per KV head.
+    running_mean: the EWMA input is the mean of all keys that have left the
+    window (the other reading of "mean(K_hist)"); state [B,Hs,2,d] = (S, M).
     Returns (out [B,n,Hq,d], ring_k, ring_v, state), all float64.
     """
     q = _np(q, np.float32)
@@ -116,23 +119,27 @@ def prefill(q, k, v, gamma, alpha, window: int, scale: float = 0.0,
     alpha = _np(np.broadcast_to(_np(alpha, np.float64), (Hq,)), np.float64)
     rk = np.zeros((B, Hkv, W, d)) if ring_k is None else _np(ring_k, np.float64).copy()
     rv = np.zeros((B, Hkv, W, d)) if ring_v is None else _np(ring_v, np.float64).copy()
-    st = np.zeros((B, Hs, d)) if state is None else _np(state, np.float64).copy()
-    assert st.shape == (B, Hs, d)
+    sshape = (B, Hs, 2, d) if running_mean else (B, Hs, d)
+    st = np.zeros(sshape) if state is None else _np(state, np.float64).copy()
+    assert st.shape == sshape
     p0 = None if pos0 is None else _np(pos0, np.int32)
     out = np.empty((B, n, Hq, d), dtype=np.float64)
     _load().oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(alpha),
                            _ptr(out), _ptr(rk), _ptr(rv), _ptr(st), _ptr(p0),
-                           B, n, Hq, Hkv, d, W, float(scale), int(bool(s_per_query)))
+                           B, n, Hq, Hkv, d, W, float(scale), int(bool(s_per_query)),
+                           int(bool(running_mean)))
     return out, rk, rv, st
 
 
 def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha,
-                scale: float = 0.0, s_per_query: bool = False):
+                scale: float = 0.0, s_per_query: bool = False, running_mean: bool = False):
     """One decode step over L layers with the W-slot ring ([P1] 2.1, 2.2).
 
     q [L,B,Hq,d]; k_new, v_new [L,B,Hkv,d]; ring_k, ring_v [L,B,Hkv,W,d];
     state [L,B,Hkv,d]; pos [B]; gamma [L,Hkv]; alpha [L,Hq].
     s_per_query: γ [L,Hq] and S [L,B,Hq,d] per query head.
+    running_mean: state [L,B,Hs,2,d] = (S, M), see prefill.
+    A negative pos[b] skips sequence b (nothing of it is written).
     Returns (out [L,B,Hq,d], ring_k, ring_v, state) as new float64 arrays.
     """
     q = _np(q, np.float32)
@@ -146,14 +153,15 @@ def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha,
     assert rk.shape == (L, B, Hkv, W, d) and rv.shape == rk.shape
     Hs = Hq if s_per_query else Hkv
     st = _np(state, np.float64).copy()
-    assert st.shape == (L, B, Hs, d)
+    assert st.shape == ((L, B, Hs, 2, d) if running_mean else (L, B, Hs, d))
     pos = _np(pos, np.int32)
     gamma = _np(np.broadcast_to(_np(gamma, np.float64), (L, Hs)), np.float64)
     alpha = _np(np.broadcast_to(_np(alpha, np.float64), (L, Hq)), np.float64)
     out = np.empty((L, B, Hq, d), dtype=np.float64)
     _load().oracle_decode_step(_ptr(q), _ptr(kn), _ptr(vn), _ptr(rk), _ptr(rv), _ptr(st),
                                _ptr(pos), _ptr(gamma), _ptr(alpha), _ptr(out),
-                               L, B, Hq, Hkv, d, W, float(scale), int(bool(s_per_query)))
+                               L, B, Hq, Hkv, d, W, float(scale), int(bool(s_per_query)),
+                               int(bool(running_mean)))
     return out, rk, rv, st
 
 

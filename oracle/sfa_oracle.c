@@ -60,15 +60,23 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
  *    head (every query head of a group folds the same evicted keys with its
  *    own decay);
  *  - query head h reads KV head h / (Hq/Hkv);
- *  - scale <= 0 means 1/sqrt(d).
+ *  - scale <= 0 means 1/sqrt(d);
+ *  - with running_mean set, the other reading of "mean(K_hist)": the EWMA
+ *    input at position p >= W is the mean M_p of all keys that have left the
+ *    window so far, positions 0..p-W (m_p = p-W+1 keys), instead of the one
+ *    key leaving at p.  The mean is kept as a running fp64 sum divided by
+ *    the count.
  *
  * Continuation: pos0[b] (NULL = all zero) is the position of the first token
  * of this call.  When pos0[b] > 0, keys and values at positions < pos0[b] are
- * read from the ring (position q in slot q mod W) and S starts from state[b].
+ * read from the ring (position q in slot q mod W) and S starts from state[b]
+ * (with running_mean, M as well: the sum restarts as M times the
+ * max(0, pos0-W) keys it averages).
  *
  * Layouts: q [B,n,Hq,d]; k, v [B,n,Hkv,d]; out [B,n,Hq,d];
  * ring_k, ring_v [B,Hkv,W,d] (in/out); state [B,Hkv,d] (in/out);
  * gamma [Hkv]; alpha [Hq].  With s_per_query: state [B,Hq,d], gamma [Hq].
+ * With running_mean: state [B,Hs,2,d], S then M.
  * ------------------------------------------------------------------------ */
 
 /* key/value of position qpos for batch b, KV head G */
@@ -86,13 +94,15 @@ void oracle_prefill(const float *q, const float *k, const float *v,
                     const double *gamma, const double *alpha,
                     double *out, double *ring_k, double *ring_v, double *state,
                     const int32_t *pos0,
-                    int B, int n, int Hq, int Hkv, int d, int W, double scale, int s_per_query) {
+                    int B, int n, int Hq, int Hkv, int d, int W, double scale, int s_per_query,
+                    int running_mean) {
     const int group = Hq / Hkv;
     const int Hs = s_per_query ? Hq : Hkv; /* heads that own an S */
+    const int sw = running_mean ? 2 * d : d; /* state words per S head */
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
-    /* final S of each (b, S head), written to state after the loop so that
+    /* final state of each (b, S head), written to state after the loop so that
      * every head reads the caller's ring/state as they were on entry */
-    double *final_S = (double *)calloc((size_t)B * Hs * d, sizeof(double));
+    double *final_S = (double *)calloc((size_t)B * Hs * sw, sizeof(double));
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b) {
@@ -102,19 +112,32 @@ void oracle_prefill(const float *q, const float *k, const float *v,
             const int p0 = pos0 ? pos0[b] : 0;
             const double g = gamma[hs];
             double *S = (double *)malloc(sizeof(double) * d);
+            double *C = (double *)malloc(sizeof(double) * d); /* running_mean: sum of the left keys */
             double *o = (double *)malloc(sizeof(double) * d);
             double *tk = (double *)malloc(sizeof(double) * d);
             double *tv = (double *)malloc(sizeof(double) * d);
             double *sc = (double *)malloc(sizeof(double) * W);
-            for (int e = 0; e < d; ++e)
-                S[e] = (p0 > 0) ? state[IDX4(0, b, hs, e, B, Hs, d)] : 0.0;
+            const double *st_in = state + ((size_t)b * Hs + hs) * sw;
+            const int m_in = (p0 - W > 0) ? p0 - W : 0; /* keys left before this call */
+            for (int e = 0; e < d; ++e) {
+                S[e] = (p0 > 0) ? st_in[e] : 0.0;
+                C[e] = (running_mean && p0 > 0) ? st_in[d + e] * m_in : 0.0;
+            }
 
             for (int t = 0; t < n; ++t) {
                 const int p = p0 + t;
                 /* far field: the key at p-W leaves the window now */
                 if (p >= W) {
                     const double *ke = kv_row(k, ring_k, b, G, p - W, p0, n, Hkv, d, W, tk);
-                    for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * ke[e];
+                    if (running_mean) {
+                        const double m = (double)(p - W + 1); /* keys left so far */
+                        for (int e = 0; e < d; ++e) {
+                            C[e] += ke[e];
+                            S[e] = g * S[e] + (1.0 - g) * (C[e] / m);
+                        }
+                    } else {
+                        for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * ke[e];
+                    }
                 }
                 /* near field: softmax over positions lo..p */
                 const int lo = (p - W + 1 > 0) ? p - W + 1 : 0;
@@ -143,9 +166,15 @@ void oracle_prefill(const float *q, const float *k, const float *v,
                 double *dst = out + IDX4(b, t, h, 0, n, Hq, d);
                 for (int e = 0; e < d; ++e) dst[e] = o[e] + alpha[h] * S[e];
             }
-            if (s_per_query || h % group == 0)
-                for (int e = 0; e < d; ++e) final_S[IDX4(0, b, hs, e, B, Hs, d)] = S[e];
-            free(S); free(o); free(tk); free(tv); free(sc);
+            if (s_per_query || h % group == 0) {
+                double *fs = final_S + ((size_t)b * Hs + hs) * sw;
+                const int m_end = (p0 + n - W > 0) ? p0 + n - W : 0;
+                for (int e = 0; e < d; ++e) {
+                    fs[e] = S[e];
+                    if (running_mean) fs[d + e] = m_end > 0 ? C[e] / m_end : 0.0;
+                }
+            }
+            free(S); free(C); free(o); free(tk); free(tv); free(sc);
         }
     }
 
@@ -164,9 +193,7 @@ void oracle_prefill(const float *q, const float *k, const float *v,
                 for (int e = 0; e < d; ++e) { rk[e] = sk[e]; rv[e] = sv[e]; }
             }
         }
-        for (int hs = 0; hs < Hs; ++hs)
-            for (int e = 0; e < d; ++e)
-                state[IDX4(0, b, hs, e, B, Hs, d)] = final_S[IDX4(0, b, hs, e, B, Hs, d)];
+        for (int i = 0; i < Hs * sw; ++i) state[(size_t)b * Hs * sw + i] = final_S[(size_t)b * Hs * sw + i];
     }
     free(final_S);
 }
@@ -186,14 +213,18 @@ void oracle_prefill(const float *q, const float *k, const float *v,
  * [L,B,Hkv,W,d] (in/out); state [L,B,Hkv,d] (in/out); pos [B];
  * gamma [L,Hkv]; alpha [L,Hq]; out [L,B,Hq,d].  With s_per_query (γ and S per
  * query head, see oracle_prefill): state [L,B,Hq,d], gamma [L,Hq]; every query
- * head folds the same evicted key into its own S.
+ * head folds the same evicted key into its own S.  With running_mean (see
+ * oracle_prefill): state [L,B,Hs,2,d], S then M; the evicted key joins the
+ * mean of the m = p-W keys that left before it, and S takes the new mean.
+ * A sequence with a negative position is skipped: nothing of it is written.
  * ------------------------------------------------------------------------ */
 void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                         double *ring_k, double *ring_v, double *state,
                         const int32_t *pos, const double *gamma, const double *alpha,
                         double *out, int L, int B, int Hq, int Hkv, int d, int W,
-                        double scale, int s_per_query) {
+                        double scale, int s_per_query, int running_mean) {
     const int group = Hq / Hkv;
+    const int sw = running_mean ? 2 * d : d; /* state words per S head */
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
     if (W > 64) return; /* the ring of [P1] §2.2 has k = 16 slots */
 
@@ -202,6 +233,7 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
         for (int b = 0; b < B; ++b) {
             for (int G = 0; G < Hkv; ++G) {
                 const int p = pos[b];
+                if (p < 0) continue;
                 const int s = p % W;
                 const size_t unit = ((size_t)l * B + b) * Hkv + G;
                 double *rk = ring_k + unit * W * d;
@@ -215,9 +247,17 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                     const size_t hs = s_per_query ? ((size_t)l * B + b) * Hq + (size_t)G * group + i : unit;
                     const double g = s_per_query ? gamma[(size_t)l * Hq + (size_t)G * group + i]
                                                  : gamma[(size_t)l * Hkv + G];
-                    double *S = state + hs * d;
-                    if (p >= W)
+                    double *S = state + hs * sw;
+                    if (p >= W && running_mean) {
+                        double *M = S + d;
+                        const double m = (double)(p - W + 1); /* keys left, this one included */
+                        for (int e = 0; e < d; ++e) {
+                            M[e] = (M[e] * (m - 1.0) + rk[(size_t)s * d + e]) / m;
+                            S[e] = g * S[e] + (1.0 - g) * M[e];
+                        }
+                    } else if (p >= W) {
                         for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
+                    }
                 }
                 for (int e = 0; e < d; ++e) {
                     rk[(size_t)s * d + e] = kn[e];
@@ -240,7 +280,7 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                     for (int j = 0; j < nvalid; ++j) { sc[j] = exp(sc[j] - m); den += sc[j]; }
                     double *dst = out + (((size_t)l * B + b) * Hq + h) * d;
                     const double a = alpha[(size_t)l * Hq + h];
-                    const double *S = state + (s_per_query ? ((size_t)l * B + b) * Hq + h : unit) * d;
+                    const double *S = state + (s_per_query ? ((size_t)l * B + b) * Hq + h : unit) * sw;
                     for (int e = 0; e < d; ++e) {
                         double o = 0.0;
                         for (int j = 0; j < nvalid; ++j) o += (sc[j] / den) * rv[(size_t)j * d + e];

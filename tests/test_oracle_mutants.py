@@ -18,20 +18,18 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "sfa_oracle.c")
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 
-DECODE_EVICT_THEN_WRITE = """                    if (p >= W)
+DECODE_EVICT_THEN_WRITE = """                    } else if (p >= W) {
                         for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
-                }
-                for (int e = 0; e < d; ++e) {
-                    rk[(size_t)s * d + e] = kn[e];
-                    rv[(size_t)s * d + e] = vn[e];
+                    }
                 }
 """
-DECODE_WRITE_THEN_EVICT = """                    for (int e = 0; e < d; ++e) {
-                        rk[(size_t)s * d + e] = kn[e];
-                        rv[(size_t)s * d + e] = vn[e];
-                    }
-                    if (p >= W)
+DECODE_WRITE_THEN_EVICT = """                    } else if (p >= W) {
+                        for (int e = 0; e < d; ++e) {
+                            rk[(size_t)s * d + e] = kn[e];
+                            rv[(size_t)s * d + e] = vn[e];
+                        }
                         for (int e = 0; e < d; ++e) S[e] = g * S[e] + (1.0 - g) * rk[(size_t)s * d + e];
+                    }
                 }
 """
 
@@ -40,6 +38,15 @@ MUTANTS = {
     "per_query_state_of_first_head_only": ("if (s_per_query || h % group == 0)", "if (h % group == 0)"),
     "per_query_decode_one_gamma": ("gamma[(size_t)l * Hq + (size_t)G * group + i]",
                                    "gamma[(size_t)l * Hq + (size_t)G * group]"),
+    "running_mean_count_off_by_one": ("const double m = (double)(p - W + 1); /* keys left so far */",
+                                      "const double m = (double)(p - W + 2); /* keys left so far */"),
+    "running_mean_ignored_in_s": ("S[e] = g * S[e] + (1.0 - g) * (C[e] / m);",
+                                  "S[e] = g * S[e] + (1.0 - g) * ke[e];"),
+    "running_mean_decode_count": ("const double m = (double)(p - W + 1); /* keys left, this one included */",
+                                  "const double m = (double)(p - W + 2); /* keys left, this one included */"),
+    "running_mean_continuation_count": ("const int m_in = (p0 - W > 0) ? p0 - W : 0;",
+                                        "const int m_in = (p0 - W + 1 > 0) ? p0 - W + 1 : 0;"),
+    "decode_negative_position_processed": ("if (p < 0) continue;", "if (p < -1000000) continue;"),
     "window_one_too_wide": ("const int lo = (p - W + 1 > 0) ? p - W + 1 : 0;",
                             "const int lo = (p - W > 0) ? p - W : 0;"),
     "evicts_wrong_key": ("kv_row(k, ring_k, b, G, p - W, p0", "kv_row(k, ring_k, b, G, p - W + 1, p0"),

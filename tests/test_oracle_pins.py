@@ -589,3 +589,148 @@ def test_per_query_continuation_equals_single_prefill(n1, n2, W):
                                     pos0=np.full(B, n1, dtype=np.int32), s_per_query=True)
     np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), full, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(st, fst, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# P13: the other reading of "mean(K_hist)" ([P1] §2.1 far-field equation): the
+# EWMA input at position t >= W is the mean of every key that has left the
+# window, positions 0..t-W, not only the key leaving at t
+# --------------------------------------------------------------------------
+def _running_mean_closed_form(k, gamma, W):
+    """S_t = (1-γ) Σ_{s=W}^{t} γ^{t-s} M_s with M_s = mean(k_0 .. k_{s-W}),
+    each mean taken directly (np.mean), each S as an explicit power sum.
+    Returns (S [n,d], M [n,d]); both 0 before t = W."""
+    n, d = k.shape
+    K = k.astype(np.float64)
+    M = np.zeros((n, d))
+    for s in range(W, n):
+        M[s] = K[: s - W + 1].mean(axis=0)
+    S = np.zeros((n, d))
+    for t in range(W, n):
+        s = np.arange(W, t + 1)
+        S[t] = ((1.0 - gamma) * gamma ** (t - s)) @ M[W: t + 1]
+    return S, M
+
+
+def _brute_force_running_mean(q, k, v, gamma, alpha, W, scale):
+    B, n, Hq, d = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    out = np.zeros((B, n, Hq, d))
+    state = np.zeros((B, Hkv, 2, d))
+    for b in range(B):
+        for G in range(Hkv):
+            K = k[b, :, G].astype(np.float64)
+            V = v[b, :, G].astype(np.float64)
+            S, M = _running_mean_closed_form(K, gamma[G], W)
+            state[b, G, 0], state[b, G, 1] = S[n - 1], M[n - 1]
+            for h in range(G * g, (G + 1) * g):
+                s = scale * (q[b, :, h].astype(np.float64) @ K.T)
+                s = np.where(_band(n, W), s, -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                out[b, :, h] = p @ V + alpha[h] * S
+    return out, state
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_running_mean_brute_force_tiny(case):
+    r = np.random.default_rng(300 + case)
+    W = int(r.integers(1, 17))
+    n = int(r.integers(1, 41))
+    d = int(r.integers(1, 9))
+    Hkv = int(r.integers(1, 3))
+    Hq = Hkv * int(r.integers(1, 4))
+    B = int(r.integers(1, 3))
+    q = r.standard_normal((B, n, Hq, d)).astype(np.float32)
+    k = r.standard_normal((B, n, Hkv, d)).astype(np.float32)
+    v = r.standard_normal((B, n, Hkv, d)).astype(np.float32)
+    gamma = r.uniform(0.0, 0.99, Hkv)
+    alpha = r.uniform(-0.5, 0.5, Hq)
+    scale = float(r.uniform(0.1, 1.0))
+    out, _, _, st = oracle.prefill(q, k, v, gamma, alpha, W, scale, running_mean=True)
+    ref, ref_st = _brute_force_running_mean(q, k, v, gamma, alpha, W, scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(st, ref_st, rtol=1e-11, atol=1e-12)
+
+
+def test_running_mean_gamma_zero_is_the_mean_of_the_left_keys():
+    """γ = 0: S_t is exactly the running mean of keys 0..t-W (a textbook mean)."""
+    B, n, H, d, W = 1, 50, 1, 5, 7
+    q, k, v = _rand((B, n, H, d)), _rand((B, n, H, d)), _rand((B, n, H, d))
+    o1, *_ = oracle.prefill(q, k, v, 0.0, 1.0, W, running_mean=True)
+    o0, *_ = oracle.prefill(q, k, v, 0.0, 0.0, W, running_mean=True)
+    S = (o1 - o0)[0, :, 0]
+    for t in range(n):
+        ref = k[0, : t - W + 1, 0].astype(np.float64).mean(axis=0) if t >= W else np.zeros(d)
+        np.testing.assert_allclose(S[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_running_mean_constant_keys():
+    """Constant keys c: every mean is c, so S_t = (1 - γ^{t-W+1}) c."""
+    B, n, H, d, W, gamma = 1, 60, 1, 3, 16, 0.9
+    c = np.array([0.5, -2.0, 3.0], dtype=np.float32)
+    k = np.broadcast_to(c, (B, n, H, d)).copy()
+    q, v = _rand((B, n, H, d)), _rand((B, n, H, d))
+    o1, *_ = oracle.prefill(q, k, v, gamma, 1.0, W, running_mean=True)
+    o0, *_ = oracle.prefill(q, k, v, gamma, 0.0, W, running_mean=True)
+    for t in range(n):
+        ref = (1.0 - gamma ** (t - W + 1)) * c.astype(np.float64) if t >= W else np.zeros(d)
+        np.testing.assert_allclose((o1 - o0)[0, t, 0], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,m,W", [(20, 5, 16), (0, 9, 4), (15, 3, 16), (7, 7, 1)])
+def test_running_mean_prefill_then_decode_equals_longer_prefill(n, m, W):
+    """P7 for the running mean: decode steps after a prefill carry (S, M)."""
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    N = n + m
+    q, k, v = _rand((B, N, Hq, d)), _rand((B, N, Hkv, d)), _rand((B, N, Hkv, d))
+    gamma, alpha = RNG.uniform(0.3, 0.99, Hkv), RNG.uniform(0, 0.5, Hq)
+    full, frk, frv, fst = oracle.prefill(q, k, v, gamma, alpha, W, running_mean=True)
+    if n > 0:
+        _, rk, rv, st = oracle.prefill(q[:, :n], k[:, :n], v[:, :n], gamma, alpha, W, running_mean=True)
+    else:
+        rk, rv, st = np.zeros((B, Hkv, W, d)), np.zeros((B, Hkv, W, d)), np.zeros((B, Hkv, 2, d))
+    for i in range(m):
+        t = n + i
+        o, rk, rv, st = oracle.decode_step(q[None, :, t], k[None, :, t], v[None, :, t],
+                                           rk[None], rv[None], st[None],
+                                           np.full(B, t, dtype=np.int32), gamma[None],
+                                           alpha[None], running_mean=True)
+        rk, rv, st = rk[0], rv[0], st[0]
+        np.testing.assert_allclose(o[0], full[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st, fst, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(rk, frk) and np.array_equal(rv, frv)
+
+
+@pytest.mark.parametrize("n1,n2,W", [(20, 13, 16), (40, 3, 4), (5, 30, 16)])
+def test_running_mean_continuation_equals_single_prefill(n1, n2, W):
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    N = n1 + n2
+    q, k, v = _rand((B, N, Hq, d)), _rand((B, N, Hkv, d)), _rand((B, N, Hkv, d))
+    gamma, alpha = RNG.uniform(0.3, 0.99, Hkv), RNG.uniform(0, 0.5, Hq)
+    full, frk, frv, fst = oracle.prefill(q, k, v, gamma, alpha, W, running_mean=True)
+    o1, rk, rv, st = oracle.prefill(q[:, :n1], k[:, :n1], v[:, :n1], gamma, alpha, W, running_mean=True)
+    o2, rk, rv, st = oracle.prefill(q[:, n1:], k[:, n1:], v[:, n1:], gamma, alpha, W,
+                                    ring_k=rk, ring_v=rv, state=st,
+                                    pos0=np.full(B, n1, dtype=np.int32), running_mean=True)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), full, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st, fst, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_negative_position_skips_the_sequence():
+    """R21: a negative pos entry leaves that sequence's ring and S untouched and
+    its outputs unwritten; the other sequences are unaffected."""
+    L, B, Hq, Hkv, d, W = 2, 3, 4, 2, 8, 16
+    dq, dk, dv = _rand((L, B, Hq, d)), _rand((L, B, Hkv, d)), _rand((L, B, Hkv, d))
+    rk, rv, st = _rand((L, B, Hkv, W, d)), _rand((L, B, Hkv, W, d)), _rand((L, B, Hkv, d))
+    gl, al = RNG.uniform(0.5, 0.99, (L, Hkv)), RNG.uniform(0, 0.5, (L, Hq))
+    pos = np.array([20, -1, 5], dtype=np.int32)
+    out, rk2, rv2, st2 = oracle.decode_step(dq, dk, dv, rk, rv, st, pos, gl, al)
+    assert np.array_equal(rk2[:, 1], rk[:, 1]) and np.array_equal(rv2[:, 1], rv[:, 1])
+    assert np.array_equal(st2[:, 1], st[:, 1])
+    keep = [0, 2]
+    ref = oracle.decode_step(dq[:, keep], dk[:, keep], dv[:, keep], rk[:, keep], rv[:, keep], st[:, keep],
+                             pos[keep], gl, al)
+    np.testing.assert_array_equal(out[:, keep], ref[0])
+    np.testing.assert_array_equal(st2[:, keep], ref[3])

@@ -203,8 +203,10 @@ def decode_per_layer_graph(bufs, steps):
 
 
 def run_variants(steps=10, warmup=2):
-    """γ and the far-field state per query head (sfa_prefill_qh, sfa_decode_step_qh):
-    one 64K-token 7B-shaped prefill layer and the 28-layer decode step."""
+    """The far-field variants: γ and S per query head (sfa_prefill_qh,
+    sfa_decode_step_qh) and the running mean of the keys that have left the
+    window (sfa_prefill_rm, sfa_decode_step_rm), each on one 64K-token 7B-shaped
+    prefill layer and the 28-layer decode step."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     res = {}
@@ -263,6 +265,64 @@ def run_variants(steps=10, warmup=2):
     ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     byts = decode_bytes() + L * Bd * (Hq - Hkv) * hd * 4 * 2
     res["decode_qh"] = {"workload": "7B-shaped decode step, 28 layers x 256 sequences, γ and S per query head",
+                        "us_per_step": ms * 1e3, "value": L * Bd * Hq / (ms * 1e-3),
+                        "unit": "tokens·heads/s (sequence, query head, layer)",
+                        "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9,
+                                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                     "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": byts}}
+    del sets
+    torch.cuda.empty_cache()
+    # running mean of the keys that have left the window (state carries S and M)
+    d = inputs.workload(4, device=dev, layer=0)
+    kw = dict(window=WIN, out=torch.empty((B, N, HQ, HD), dtype=torch.bfloat16, device=dev),
+              ring_k=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
+              ring_v=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
+              state=torch.zeros((B, HKV, 2, HD), dtype=torch.float32, device=dev),
+              workspace=torch.empty(sfa.prefill_workspace_size(B, N, 3 * HKV, HD), dtype=torch.uint8,
+                                    device=dev),
+              stream=stream, running_mean=True)
+    for _ in range(warmup):
+        sfa.prefill(d["q"], d["k"], d["v"], d["gamma"], d["alpha"], **kw)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        sfa.prefill(d["q"], d["k"], d["v"], d["gamma"], d["alpha"], **kw)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    byts = prefill_bytes_per_launch() + B * HKV * HD * 4
+    res["prefill_rm"] = {"workload": "7B-shaped 64K-token prefill layer, running mean of the keys that left the window",
+                         "us_per_call": ms * 1e3, "value": B * N * HQ / (ms * 1e-3),
+                         "unit": "tokens·heads/s",
+                         "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9,
+                                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                      "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_call": byts}}
+    del d, kw
+    torch.cuda.empty_cache()
+    sets = []
+    for i in range(3):
+        dd = inputs.decode_inputs(L, Bd, Hq, Hkv, hd, seed=4300 + i, device=dev)
+        dd["state"] = inputs.normal((L, Bd, Hkv, 2, hd), 4400 + i, 1.0, torch.float32, dev)
+        dd["out"] = torch.empty((L, Bd, Hq, hd), dtype=torch.bfloat16, device=dev)
+        sets.append(dd)
+
+    def call_rm(dd):
+        sfa.decode_step(dd["q"], dd["k_new"], dd["v_new"], dd["ring_k"], dd["ring_v"], dd["state"],
+                        dd["pos"], dd["gamma"], dd["alpha"], out=dd["out"], stream=stream, running_mean=True)
+
+    for i in range(3):
+        call_rm(sets[i % 3])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        call_rm(sets[i % 3])
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    byts = decode_bytes() + L * Bd * Hkv * hd * 4 * 2
+    res["decode_rm"] = {"workload": "7B-shaped decode step, 28 layers x 256 sequences, running mean",
                         "us_per_step": ms * 1e3, "value": L * Bd * Hq / (ms * 1e-3),
                         "unit": "tokens·heads/s (sequence, query head, layer)",
                         "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9,

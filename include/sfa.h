@@ -158,6 +158,27 @@ int sfa_prefill_qh(const void *q, const void *k, const void *v,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sfa_prefill_rm -- sfa_prefill under the other reading of "mean(K_hist)" in
+ * the first page's section 2.1 far-field equation: at a position p >= W the
+ * EWMA input is the mean M_p of every key that has left the window so far
+ * (positions 0..p-W, m = p-W+1 keys), not only the key leaving at p:
+ *   S_p = γ·S_{p-1} + (1-γ)·M_p,   O = O_near + α·S_p.
+ * S and γ are per KV head; the near field and the ring are those of
+ * sfa_prefill.
+ *  state    [B,Hkv,2,d] fp32: S, then M (written; read first when pos0 != NULL,
+ *           M then standing for the max(0, pos0-W) keys that left before).
+ *  workspace at least sfa_prefill_workspace_size(B, n, 3*Hkv, d) bytes.
+ * Every other argument, layout and error code is that of sfa_prefill.
+ */
+int sfa_prefill_rm(const void *q, const void *k, const void *v,
+                   const float *gamma, const float *alpha,
+                   void *out, void *ring_k, void *ring_v, float *state,
+                   const int32_t *pos0,
+                   int B, int n, int Hq, int Hkv, int d, int window, float scale,
+                   int in_dtype, int out_dtype,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * sfa_decode_step -- one generated token for L layers at once.
  * (First page, section 2.1 equations with the constant-memory k-slot ring of
  * section 2.2.)
@@ -193,6 +214,20 @@ int sfa_decode_step(const void *q, const void *k_new, const void *v_new,
  * Every other argument, layout and error code is that of sfa_decode_step.
  */
 int sfa_decode_step_qh(const void *q, const void *k_new, const void *v_new,
+                       void *ring_k, void *ring_v, float *state,
+                       const int32_t *pos, const float *gamma, const float *alpha,
+                       void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale,
+                       int in_dtype, int out_dtype, void *stream);
+
+/*
+ * sfa_decode_step_rm -- sfa_decode_step with the running mean of the keys
+ * that have left the window as the EWMA input (see sfa_prefill_rm): when the
+ * key of position pos-W leaves, M <- (M·(m-1) + k)/m with m = pos-W+1, then
+ * S <- γ·S + (1-γ)·M.
+ *  state  [L,B,Hkv,2,d] fp32 (in/out): S, then M.
+ * Every other argument, layout and error code is that of sfa_decode_step.
+ */
+int sfa_decode_step_rm(const void *q, const void *k_new, const void *v_new,
                        void *ring_k, void *ring_v, float *state,
                        const int32_t *pos, const float *gamma, const float *alpha,
                        void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale,

@@ -17,8 +17,9 @@ SFA_PREFILL_SCAN, SFA_PREFILL_ATTEND = 1, 2
 
 # every symbol include/sfa.h declares
 EXPORTS = ("sfa_status_string", "sfa_abi_version", "sfa_prefill_workspace_size", "sfa_prefill",
-           "sfa_prefill_part", "sfa_prefill_qh",
-           "sfa_decode_step", "sfa_decode_step_qh", "sfa_enhance_workspace_size", "sfa_enhance")
+           "sfa_prefill_part", "sfa_prefill_qh", "sfa_prefill_rm",
+           "sfa_decode_step", "sfa_decode_step_qh", "sfa_decode_step_rm", "sfa_enhance_workspace_size",
+           "sfa_enhance")
 
 _lib = None
 
@@ -51,10 +52,14 @@ def lib() -> ctypes.CDLL:
         L.sfa_prefill_part.restype = I
         L.sfa_prefill_qh.argtypes = L.sfa_prefill.argtypes
         L.sfa_prefill_qh.restype = I
+        L.sfa_prefill_rm.argtypes = L.sfa_prefill.argtypes
+        L.sfa_prefill_rm.restype = I
         L.sfa_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
         L.sfa_decode_step.restype = I
         L.sfa_decode_step_qh.argtypes = L.sfa_decode_step.argtypes
         L.sfa_decode_step_qh.restype = I
+        L.sfa_decode_step_rm.argtypes = L.sfa_decode_step.argtypes
+        L.sfa_decode_step_rm.restype = I
         L.sfa_enhance_workspace_size.argtypes = [I, I, I]
         L.sfa_enhance_workspace_size.restype = Z
         L.sfa_enhance.argtypes = [P, P, P, P, P, ctypes.c_longlong, P, I, I, I, I, I, I,

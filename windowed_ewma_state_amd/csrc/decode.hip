@@ -81,9 +81,12 @@ template <typename T> struct Vec<T, 2> {
     }
 };
 
-// QH: γ and S per query head (state [L,B,Hq,d], gamma [L,Hq])
-template <typename TIn, typename TOut, int D, bool QH>
+// MODE (far-field variant): kKvHead, kQueryHead (γ and S per query head:
+// state [L,B,Hq,d], gamma [L,Hq]) or kRunningMean (state [L,B,Hkv,2,d]: S and
+// the mean M of the keys that have left the window, which is the EWMA input)
+template <typename TIn, typename TOut, int D, int MODE>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
+    constexpr bool QH = MODE == kQueryHead, RM = MODE == kRunningMean;
     constexpr int EPL = D / kWave;
     __shared__ float4 P_lds[kUnitsPerBlock][16][4];  // [unit][head in tile][slots/4]
 
@@ -111,14 +114,15 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     const TIn *kn = reinterpret_cast<const TIn *>(a.k_new) + unit * D;
     const TIn *vn = reinterpret_cast<const TIn *>(a.v_new) + unit * D;
     const TIn *qg = reinterpret_cast<const TIn *>(a.q) + (lb * a.Hq + (long)G * group) * D;
-    float *S_ptr = a.state + unit * D;
+    float *S_ptr = a.state + unit * (RM ? 2 * D : D);
     const int e0 = lane * EPL;
 
     // ---- issue the unit's loads -------------------------------------------
-    float S[EPL], kev[EPL];
+    float S[EPL], M[EPL], kev[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) S[e] = kev[e] = 0.f;
+    for (int e = 0; e < EPL; ++e) S[e] = M[e] = kev[e] = 0.f;
     if constexpr (!QH) Vec<float, EPL>::load(S_ptr + e0, S);
+    if constexpr (RM) Vec<float, EPL>::load(S_ptr + D + e0, M);
     const bool evict = p >= W;
     if (evict) Vec<TIn, EPL>::load(ringK + (long)s * D + e0, kev);
 
@@ -137,8 +141,17 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     // ---- far field: the key of position p-W leaves the window -------------
     if (!QH && evict) {
         const float gm = a.gamma[(long)l * a.Hkv + G];
+        if constexpr (RM) {  // the key joins the mean of the p-W keys that left before it
+            const float mf = (float)(p - W + 1);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kev[e];
+            for (int e = 0; e < EPL; ++e) {
+                M[e] += (kev[e] - M[e]) / mf;
+                S[e] = gm * S[e] + (1.f - gm) * M[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kev[e];
+        }
     }
 
     // ---- near field, 16 heads of the group per MFMA tile --------------------
@@ -207,6 +220,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 
     // ---- cache update (after every read of the unit's ring) -----------------
     if constexpr (!QH) Vec<float, EPL>::store(S_ptr + e0, S);
+    if constexpr (RM) Vec<float, EPL>::store(S_ptr + D + e0, M);
     Vec<TIn, EPL>::copy(ringK + (long)s * D + e0, kn + e0);
     Vec<TIn, EPL>::copy(ringV + (long)s * D + e0, vn + e0);
 }
@@ -251,7 +265,7 @@ struct UnitLoads {
     // QN query instructions cover QN * RPI heads: half the register space
     // when the group has at most 8 heads
     u32x4 k[NI], q[QN], v[NI];
-    float S[EPL];
+    float S[EPL], M[EPL];  // S (and with the running mean, M) of the unit
     uint32_t kn, vn;  // this lane's head-dim elements of k_new / v_new (raw bits)
     float gm;         // γ of the unit's S (per query head: of head c16)
     float al;         // α of head c16 (0 past the group)
@@ -260,8 +274,9 @@ struct UnitLoads {
 
 // `live` false: the loop's last prefetch, issued anyway (see k_decode_mfma)
 // with every lane of an instruction at one 16-byte chunk of the unit.
-template <int D, int QN, bool QH>
+template <int D, int QN, int MODE>
 __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoads<D, QN> &u, int lane, bool live) {
+    constexpr bool QH = MODE == kQueryHead, RM = MODE == kRunningMean;
     using U = UnitLoads<D, QN>;
     constexpr int EPL = D / kWave;
     const int G = unit % a.Hkv;
@@ -307,9 +322,13 @@ __device__ __forceinline__ void unit_load(const DecodeArgs &a, int unit, UnitLoa
     // far-field state, new key/value (e-pair layout: lane owns d = EPL*lane ..)
     const int e0 = live ? lane * EPL : 0;
     if constexpr (!QH) {  // (per query head, the compute step reads its heads' S)
-        const float *S_ptr = a.state + (long)unit * D + e0;
+        const float *S_ptr = a.state + (long)unit * (RM ? 2 * D : D) + e0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) u.S[e] = S_ptr[e];
+        if constexpr (RM) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) u.M[e] = S_ptr[D + e];
+        }
     }
     if (EPL == 2) {
         u.kn = *reinterpret_cast<const uint32_t *>(kn + e0);
@@ -349,10 +368,11 @@ __device__ __forceinline__ T *sink_or(T *p, bool skip, int lane) {
     return skip ? reinterpret_cast<T *>(g_decode_sink + 4 * lane) : p;
 }
 
-template <typename TOut, int D, int QN, bool QH>
+template <typename TOut, int D, int QN, int MODE>
 __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, const UnitLoads<D, QN> &u,
-                                             const LateLoads<D, QH> &late, int lane, __bf16 *vt, float *sl,
-                                             __bf16 *kqt) {
+                                             const LateLoads<D, MODE == kQueryHead> &late, int lane,
+                                             __bf16 *vt, float *sl, __bf16 *kqt) {
+    constexpr bool QH = MODE == kQueryHead, RM = MODE == kRunningMean;
     constexpr int EPL = D / kWave;
     constexpr int VTS = kMaxWindow + 4;
     const int q4 = lane >> 4, c16 = lane & 15;
@@ -410,11 +430,20 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
         } else {
             kev[0] = bf16_bits_to_f32(krow_s[e0]);
         }
-        float S[EPL];
+        float S[EPL], M[EPL];
         if constexpr (!QH) {
             const float gm = u.gm;
+            if constexpr (RM) {  // the key joins the mean of the p-W keys that left before it
+                const float mf = (float)(p - W + 1);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * kev[e] : u.S[e];
+                for (int e = 0; e < EPL; ++e) {
+                    M[e] = (p >= W) ? u.M[e] + (kev[e] - u.M[e]) / mf : u.M[e];
+                    S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * M[e] : u.S[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) S[e] = (p >= W) ? gm * u.S[e] + (1.f - gm) * kev[e] : u.S[e];
+            }
 #pragma unroll
             for (int e = 0; e < EPL; ++e) sl[e0 + e] = S[e];
         }
@@ -538,11 +567,14 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
                 for (int half = 0; half < 2; ++half)
                     *sink_or(reinterpret_cast<f32x4 *>(Sg + 32 * k + 4 * half), skip, lane) = Sq[k][half];
         } else {
-            float *S_ptr = a.state + (long)unit * D + e0;
+            float *S_ptr = a.state + (long)unit * (RM ? 2 * D : D) + e0;
             if constexpr (EPL == 2) {
                 *sink_or(reinterpret_cast<float2 *>(S_ptr), skip, lane) = make_float2(S[0], S[EPL - 1]);
+                if constexpr (RM)
+                    *sink_or(reinterpret_cast<float2 *>(S_ptr + D), skip, lane) = make_float2(M[0], M[EPL - 1]);
             } else {
                 *sink_or(S_ptr, skip, lane) = S[0];
+                if constexpr (RM) *sink_or(S_ptr + D, skip, lane) = M[0];
             }
         }
         __bf16 *ringK = sink_or(reinterpret_cast<__bf16 *>(a.ring_k) + ((long)unit * W + s) * D + e0, skip, lane);
@@ -558,8 +590,9 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
     }
 }
 
-template <typename TOut, int D, int QN, bool QH>
+template <typename TOut, int D, int QN, int MODE>
 __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
+    constexpr bool QH = MODE == kQueryHead;
     constexpr int VTS = kMaxWindow + 4;  // V^T row stride (bf16): 16 slots + pad
     __shared__ __attribute__((aligned(16))) __bf16 Vt[4][D * VTS];
     __shared__ __attribute__((aligned(16))) float Sl[4][D];
@@ -585,26 +618,26 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(DecodeArgs a) {
     if (unit >= n_units) return;
     UnitLoads<D, QN> A, Bf;
     LateLoads<D, QH> late;
-    unit_load<D, QN, QH>(a, unit, A, lane, true);
+    unit_load<D, QN, MODE>(a, unit, A, lane, true);
     int next = unit + stride;
     bool more = next < n_units;
     late_load<D, QH>(a, unit, late, lane);
-    unit_load<D, QN, QH>(a, more ? next : unit, Bf, lane, more);
-    unit_compute<TOut, D, QN, QH>(a, unit, A, late, lane, vt, sl, kqt);
+    unit_load<D, QN, MODE>(a, more ? next : unit, Bf, lane, more);
+    unit_compute<TOut, D, QN, MODE>(a, unit, A, late, lane, vt, sl, kqt);
     while (more) {
         unit = next;
         next = unit + stride;
         more = next < n_units;
         late_load<D, QH>(a, unit, late, lane);
-        unit_load<D, QN, QH>(a, more ? next : unit, A, lane, more);
-        unit_compute<TOut, D, QN, QH>(a, unit, Bf, late, lane, vt, sl, kqt);
+        unit_load<D, QN, MODE>(a, more ? next : unit, A, lane, more);
+        unit_compute<TOut, D, QN, MODE>(a, unit, Bf, late, lane, vt, sl, kqt);
         if (!more) break;
         unit = next;
         next = unit + stride;
         more = next < n_units;
         late_load<D, QH>(a, unit, late, lane);
-        unit_load<D, QN, QH>(a, more ? next : unit, Bf, lane, more);
-        unit_compute<TOut, D, QN, QH>(a, unit, A, late, lane, vt, sl, kqt);
+        unit_load<D, QN, MODE>(a, more ? next : unit, Bf, lane, more);
+        unit_compute<TOut, D, QN, MODE>(a, unit, A, late, lane, vt, sl, kqt);
     }
 }
 
@@ -635,7 +668,7 @@ hipError_t launch_persistent(K kernel, const DecodeArgs &a, long units, hipStrea
     return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, bool QH>
+template <typename TIn, typename TOut, int MODE>
 hipError_t launch_q(const DecodeArgs &a, hipStream_t stream) {
     const long units = (long)a.L * a.B * a.Hkv;
     if constexpr (std::is_same<TIn, __bf16>::value) {
@@ -643,23 +676,25 @@ hipError_t launch_q(const DecodeArgs &a, hipStream_t stream) {
             // query rows per load instruction: 4 (d 128) or 8 (d 64)
             const bool half = a.group <= 8;
             if (a.d == 128)
-                return half ? launch_persistent(k_decode_mfma<TOut, 128, 2, QH>, a, units, stream)
-                            : launch_persistent(k_decode_mfma<TOut, 128, 4, QH>, a, units, stream);
-            return half ? launch_persistent(k_decode_mfma<TOut, 64, 1, QH>, a, units, stream)
-                        : launch_persistent(k_decode_mfma<TOut, 64, 2, QH>, a, units, stream);
+                return half ? launch_persistent(k_decode_mfma<TOut, 128, 2, MODE>, a, units, stream)
+                            : launch_persistent(k_decode_mfma<TOut, 128, 4, MODE>, a, units, stream);
+            return half ? launch_persistent(k_decode_mfma<TOut, 64, 1, MODE>, a, units, stream)
+                        : launch_persistent(k_decode_mfma<TOut, 64, 2, MODE>, a, units, stream);
         }
     }
     const dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock));
     if (a.d == 128)
-        hipLaunchKernelGGL((k_decode<TIn, TOut, 128, QH>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_decode<TIn, TOut, 128, MODE>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_decode<TIn, TOut, 64, QH>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_decode<TIn, TOut, 64, MODE>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 template <typename TIn, typename TOut>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
-    return a.s_per_query ? launch_q<TIn, TOut, true>(a, stream) : launch_q<TIn, TOut, false>(a, stream);
+    if (a.s_per_query) return launch_q<TIn, TOut, kQueryHead>(a, stream);
+    if (a.running_mean) return launch_q<TIn, TOut, kRunningMean>(a, stream);
+    return launch_q<TIn, TOut, kKvHead>(a, stream);
 }
 
 }  // namespace

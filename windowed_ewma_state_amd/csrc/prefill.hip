@@ -56,8 +56,14 @@ __device__ __forceinline__ void load_epl(const T *p, float *x) {
 // One wave per 64-token tile of one (b, KV head) chain (four chains per workgroup).  Lane (w, c) owns the
 // 16-byte chunk c of the head dimension for block w of the tile, so every load
 // is a 16-byte vector and a block's 16 rows are in flight together.
+//
+// RM (running mean of the keys that have left the window): a segment maps the
+// incoming (S, C) to g·S + β·C + s and C + c, with g = γ^(evicting steps), c
+// the sum of the keys it evicts, s its S from (0, 0) and β = Σ over its
+// evicting steps of (1-γ)·γ^(later evicting steps)/m; m = p-W+1 at position p.
+// The kernel writes s and c per block and tile and β per tile.
 // ---------------------------------------------------------------------------
-template <typename TIn, int D>
+template <typename TIn, int D, bool RM>
 __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     constexpr int EPC = 16 / sizeof(TIn);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;           // chunks per row (8 or 16 for bf16, 16 or 32 for fp32)
@@ -83,11 +89,17 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     const int tb = tile * kTile + kBlk * blk;
     const bool lane_ok = c0 < CPR;  // d = 64 bf16 has 8 chunks per row: half the lanes idle
 
-    float A[CPL][EPC];
+    float A[CPL][EPC], Cs[RM ? CPL : 1][EPC];
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) A[cc][e] = 0.f;
+    if constexpr (RM) {
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) Cs[cc][e] = 0.f;
+    }
     if (lane_ok) {
         u32x4 raw[kBlk][CPL];
         bool use[kBlk];
@@ -105,6 +117,7 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < kBlk; ++j) {
             if (!use[j]) continue;
+            const float inv_m = RM ? 1.f / (float)(p0 + tb + j - W + 1) : 0.f;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 float v[EPC];
@@ -118,42 +131,88 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(raw[j][cc][i]);
                 }
+                if constexpr (RM) {
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) A[cc][e] = gm * A[cc][e] + (1.f - gm) * v[e];
+                    for (int e = 0; e < EPC; ++e) {
+                        Cs[cc][e] += v[e];
+                        A[cc][e] = gm * A[cc][e] + (1.f - gm) * (Cs[cc][e] * inv_m);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) A[cc][e] = gm * A[cc][e] + (1.f - gm) * v[e];
+                }
             }
         }
     }
     // 16-token block aggregates, then the tile aggregate: blocks combined in
     // order through LDS, T = ((A0·g1 + A1)·g2 + A2)·g3 + A3 with g_w the decay
-    // over block w's evicting steps
+    // over block w's evicting steps (RM: T = g_w·T + β_w·TC + A_w, TC += C_w)
     float *a16 = a.agg16 + (((long)bg * a.ntiles + tile) * 4 + blk) * D;
     const int blen = max(0, min(kBlk, n - tb));
     const int steps = max(0, blen - max(0, W - p0 - tb));
     const float gl = powi(gm, steps);
+    float bw = 0.f;  // RM: β of this lane's block
+    if constexpr (RM) {
+        for (int j = 0; j < blen; ++j) {
+            const int p = p0 + tb + j;
+            if (p >= W) bw = gm * bw + (1.f - gm) / (float)(p - W + 1);
+        }
+    }
     if (lane_ok) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
             for (int e = 0; e < EPC; ++e) a16[(c0 + LPB * cc) * EPC + e] = A[cc][e];
+        if constexpr (RM) {
+            float *c16 = a.csum16 + (((long)bg * a.ntiles + tile) * 4 + blk) * D;
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) c16[(c0 + LPB * cc) * EPC + e] = Cs[cc][e];
+        }
     }
     __shared__ float blkv[4][4][D];  // [wave][block][d]
+    __shared__ float blkc[RM ? 4 : 1][4][RM ? D : 1];
     if (lane_ok) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) blkv[wave][blk][(c0 + LPB * cc) * EPC + e] = A[cc][e];
+            for (int e = 0; e < EPC; ++e) {
+                blkv[wave][blk][(c0 + LPB * cc) * EPC + e] = A[cc][e];
+                if constexpr (RM) blkc[wave][blk][(c0 + LPB * cc) * EPC + e] = Cs[cc][e];
+            }
     }
-    __shared__ float decay[4][4];
-    if (c0 == 0) decay[wave][blk] = gl;
+    __shared__ float decay[4][4], beta[4][4];
+    if (c0 == 0) {
+        decay[wave][blk] = gl;
+        beta[wave][blk] = bw;
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float *a64 = a.agg64 + ((long)bg * a.ntiles + tile) * D;
+    const long trec = (long)bg * a.ntiles + tile;
+    float *a64 = a.agg64 + trec * D;
     for (int e = lane; e < D; e += 64) {
-        float T = 0.f;
+        float T = 0.f, TC = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) T = decay[wave][w] * T + blkv[wave][w][e];
+        for (int w = 0; w < 4; ++w) {
+            if constexpr (RM) {
+                T = decay[wave][w] * T + beta[wave][w] * TC + blkv[wave][w][e];
+                TC += blkc[wave][w][e];
+            } else {
+                T = decay[wave][w] * T + blkv[wave][w][e];
+            }
+        }
         a64[e] = T;
+        if constexpr (RM) a.csum64[trec * D + e] = TC;
+    }
+    if constexpr (RM) {
+        if (lane == 0) {
+            float Bt = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) Bt = decay[wave][w] * Bt + beta[wave][w];
+            a.beta64[trec] = Bt;
+        }
     }
 }
 
@@ -172,9 +231,15 @@ __device__ __forceinline__ int evict_steps(int p0, int s0, int len, int W) {
 // ---------------------------------------------------------------------------
 constexpr int kCarryParts = 64, kCarryCols = 16;
 
+// RM: the same scan over the affine maps (g, β, s, c) of the tiles, carrying
+// (S, C); parts compose as (G, B, X, Cx) then (g, β, s, c) ->
+// (g·G, g·B + β, g·X + β·Cx + s, Cx + c).  It also writes C before each tile
+// and the final mean C/m.
+template <bool RM>
 __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
     __shared__ float partX[kCarryParts][kCarryCols];
-    __shared__ float partG[kCarryParts];
+    __shared__ float partC[RM ? kCarryParts : 1][kCarryCols];
+    __shared__ float partG[kCarryParts], partB[kCarryParts];
     const int D = a.d;
     const int cblocks = D / kCarryCols;
     const int bg = blockIdx.x / cblocks;
@@ -184,52 +249,98 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
     const int n = a.n, W = a.W, nt = a.ntiles;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
     const float gm = a.gamma[hs];
-    const float S_init = (a.pos0 && p0 > 0) ? a.state[(long)bg * D + e] : 0.f;
+    const long sw = RM ? 2L * D : (long)D;  // state words per chain
+    const float S_init = (a.pos0 && p0 > 0) ? a.state[(long)bg * sw + e] : 0.f;
+    // RM: the key sum restarts as the carried mean times the keys it averages
+    const float C_init = (RM && a.pos0 && p0 > 0) ? a.state[(long)bg * sw + D + e] * (float)max(0, p0 - W) : 0.f;
     const float g64 = powi(gm, kTile);
 
     const int per = (nt + kCarryParts - 1) / kCarryParts;
     const int i0 = min(part * per, nt), i1 = min(i0 + per, nt);
     const float *A = a.agg64 + (long)bg * nt * D + e;
+    const float *Cs = RM ? a.csum64 + (long)bg * nt * D + e : nullptr;
+    const float *Bt = RM ? a.beta64 + (long)bg * nt : nullptr;
     auto decay_of = [&](int i) {
         const int len = min(kTile, n - i * kTile);
         const int st = evict_steps(p0, i * kTile, len, W);
         return st == kTile ? g64 : powi(gm, st);
     };
-    float X = 0.f, Gam = 1.f;
+    float X = 0.f, Gam = 1.f, Bc = 0.f, Cx = 0.f;
 #pragma unroll 8
     for (int i = i0; i < i1; ++i) {
         const float gl = decay_of(i);
-        X = gl * X + A[(long)i * D];
+        if constexpr (RM) {
+            const float be = Bt[i];
+            X = gl * X + be * Cx + A[(long)i * D];
+            Cx += Cs[(long)i * D];
+            Bc = gl * Bc + be;
+        } else {
+            X = gl * X + A[(long)i * D];
+        }
         Gam *= gl;
     }
-    // inclusive scan of the part aggregates (X, Γ) over parts, log2(parts) steps:
+    // inclusive scan of the part aggregates over parts, log2(parts) steps:
     // (X_a, Γ_a) then (X_b, Γ_b) combine to (Γ_b·X_a + X_b, Γ_a·Γ_b)
+    // (RM: X = Γ_b·X_a + B_b·Cx_a + X_b, Cx = Cx_a + Cx_b, B = Γ_b·B_a + B_b)
     const int col = threadIdx.x % kCarryCols;
 #pragma unroll
     for (int off = 1; off < kCarryParts; off <<= 1) {
         partX[part][col] = X;
-        if (col == 0) partG[part] = Gam;
+        if constexpr (RM) partC[part][col] = Cx;
+        if (col == 0) {
+            partG[part] = Gam;
+            partB[part] = Bc;
+        }
         __syncthreads();
         if (part >= off) {
-            X = Gam * partX[part - off][col] + X;
+            if constexpr (RM) {
+                X = Gam * partX[part - off][col] + Bc * partC[part - off][col] + X;
+                Cx = partC[part - off][col] + Cx;
+                Bc = Gam * partB[part - off] + Bc;
+            } else {
+                X = Gam * partX[part - off][col] + X;
+            }
             Gam = partG[part - off] * Gam;
         }
         __syncthreads();
     }
     partX[part][col] = X;
-    if (col == 0) partG[part] = Gam;
+    if constexpr (RM) partC[part][col] = Cx;
+    if (col == 0) {
+        partG[part] = Gam;
+        partB[part] = Bc;
+    }
     __syncthreads();
-    // carry into this part: S_init through all earlier parts
-    float C = S_init;
-    if (part > 0) C = partG[part - 1] * S_init + partX[part - 1][col];
+    // carry into this part: (S_init, C_init) through all earlier parts
+    float C = S_init, K = C_init;
+    if (part > 0) {
+        C = partG[part - 1] * S_init + partX[part - 1][col];
+        if constexpr (RM) {
+            C += partB[part - 1] * C_init;
+            K = C_init + partC[part - 1][col];
+        }
+    }
     float *Cout = a.carry + (long)bg * nt * D + e;
+    float *Kout = RM ? a.ccarry + (long)bg * nt * D + e : nullptr;
     X = C;
 #pragma unroll 8
     for (int i = i0; i < i1; ++i) {
         Cout[(long)i * D] = X;
-        X = decay_of(i) * X + A[(long)i * D];
+        if constexpr (RM) {
+            Kout[(long)i * D] = K;
+            X = decay_of(i) * X + Bt[i] * K + A[(long)i * D];
+            K += Cs[(long)i * D];
+        } else {
+            X = decay_of(i) * X + A[(long)i * D];
+        }
     }
-    if (part == kCarryParts - 1 && a.state) a.state[(long)bg * D + e] = X;
+    if (part == kCarryParts - 1 && a.state) {
+        a.state[(long)bg * sw + e] = X;
+        if constexpr (RM) {
+            const int m_end = max(0, p0 + n - W);
+            a.state[(long)bg * sw + D + e] = m_end > 0 ? K / (float)m_end : 0.f;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -278,8 +389,12 @@ __device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float *v) {
 
 // QH: γ and S per query head (scan chains (b, query head)); each head's S tile
 // is rebuilt in the head loop from its carry and the wave's evicted keys.
-template <typename TIn, typename TOut, int D, bool QH>
+// RM: the running mean of the keys that have left the window is the EWMA
+// input; the wave starts from the tile's carried (S, C) and the block
+// aggregates of its earlier blocks, then scans C += k, S = γS + (1-γ)·C/m.
+template <typename TIn, typename TOut, int D, int MODE>
 __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
+    constexpr bool QH = MODE == kQueryHead, RM = MODE == kRunningMean;
     constexpr bool kBf16 = std::is_same<TIn, __bf16>::value;
     constexpr int EPL = D / kWave;
     constexpr int KS = D + Lds<TIn>::kpad;      // Klds row stride (elements)
@@ -366,6 +481,17 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     const long chain0 = QH ? (long)b * a.Hq + (long)G * group : (long)bg;
     float Cin[EPL], Ain[3][EPL];
     carry_loads(chain0, Cin, Ain);
+    // RM: the key sum carried into the tile and the earlier blocks' key sums
+    float Kin[RM ? EPL : 1], Kblk[RM ? 3 : 1][RM ? EPL : 1];
+    if constexpr (RM) {
+        const long tbase = chain0 * a.ntiles + tile;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) Kin[e] = a.ccarry[tbase * D + e0 + e];
+#pragma unroll
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) Kblk[w][e] = a.csum16[(tbase * 4 + w) * D + e0 + e];
+    }
 
     // ---- (1) stage K rows (row-major) and V (transposed) ---------------------
     // Every load of the staging is issued before the first LDS write, so the
@@ -497,8 +623,36 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // staging area is reused in the head loop)
     float kev[QH ? kBlk : 1][EPL];
     if constexpr (!QH) {
-        float S[EPL];
-        block_start(gm, Cin, Ain, S);
+        float S[EPL], Ck[RM ? EPL : 1];
+        if constexpr (RM) {
+            // (S, C) at the block start: each earlier block w maps them to
+            // g_w·S + β_w·C + A_w and C + K_w
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                S[e] = Cin[e];
+                Ck[e] = Kin[e];
+            }
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                if (w < wave) {
+                    const int s0 = t0 + kBlk * w;
+                    const int len = min(kBlk, n - s0);
+                    const float gl = powi(gm, evict_steps(p0, s0, len, W));
+                    float bw = 0.f;
+                    for (int j = 0; j < len; ++j) {
+                        const int p = p0 + s0 + j;
+                        if (p >= W) bw = gm * bw + (1.f - gm) / (float)(p - W + 1);
+                    }
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        S[e] = gl * S[e] + bw * Ck[e] + Ain[w][e];
+                        Ck[e] += Kblk[w][e];
+                    }
+                }
+            }
+        } else {
+            block_start(gm, Cin, Ain, S);
+        }
         __syncthreads();
 
         // ---- (3) EWMA through the block: S_t after token t's own eviction -----
@@ -510,8 +664,17 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
                 const TIn *kr = &Klds[(kBlk * wave + j + kMaxWindow - W) * KS + e0];
                 float kv[EPL];
                 load_epl<TIn, EPL>(kr, kv);
+                if constexpr (RM) {
+                    const float inv_m = 1.f / (float)(p0 + t - W + 1);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kv[e];
+                    for (int e = 0; e < EPL; ++e) {
+                        Ck[e] += kv[e];
+                        S[e] = gm * S[e] + (1.f - gm) * (Ck[e] * inv_m);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) S[e] = gm * S[e] + (1.f - gm) * kv[e];
+                }
             }
 #pragma unroll
             for (int e = 0; e < EPL; ++e) Sw[j * SS + e0 + e] = S[e];
@@ -787,14 +950,22 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t stream, int parts) {
     const unsigned tiles = (unsigned)(a.B * a.Hkv * a.ntiles);
     if (parts & kPrefillScan) {
         const unsigned scan_tiles = (unsigned)(a.B * a.Hs * a.ntiles);
-        hipLaunchKernelGGL((k_ewma_agg<TIn, D>), dim3((scan_tiles + 3) / 4), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(k_ewma_carry, dim3(a.B * a.Hs * (D / kCarryCols)), dim3(1024), 0, stream, a);
+        const dim3 agg_grid((scan_tiles + 3) / 4), carry_grid(a.B * a.Hs * (D / kCarryCols));
+        if (a.running_mean) {
+            hipLaunchKernelGGL((k_ewma_agg<TIn, D, true>), agg_grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(k_ewma_carry<true>, carry_grid, dim3(1024), 0, stream, a);
+        } else {
+            hipLaunchKernelGGL((k_ewma_agg<TIn, D, false>), agg_grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(k_ewma_carry<false>, carry_grid, dim3(1024), 0, stream, a);
+        }
     }
     if (parts & kPrefillAttend) {
         if (a.s_per_query)
-            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, true>), dim3(tiles), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kQueryHead>), dim3(tiles), dim3(256), 0, stream, a);
+        else if (a.running_mean)
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kRunningMean>), dim3(tiles), dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, false>), dim3(tiles), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kKvHead>), dim3(tiles), dim3(256), 0, stream, a);
         if (a.pos0 && a.ring_k)
             hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
     }

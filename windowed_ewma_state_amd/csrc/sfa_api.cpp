@@ -43,8 +43,9 @@ size_t sfa_prefill_workspace_size(int B, int n, int Hkv, int d) {
 
 namespace {
 
-// one prefill call; s_per_query selects γ and S per query head (Hs = Hq)
-int prefill_impl(int parts, int s_per_query, const void *q, const void *k, const void *v,
+// one prefill call; mode: sfa::kKvHead, kQueryHead (γ and S per query head,
+// Hs = Hq) or kRunningMean (state [B,Hkv,2,d], three times the workspace)
+int prefill_impl(int parts, int mode, const void *q, const void *k, const void *v,
                  const float *gamma, const float *alpha, void *out, void *ring_k, void *ring_v,
                  float *state, const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
                  float scale, int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes,
@@ -62,8 +63,10 @@ int prefill_impl(int parts, int s_per_query, const void *q, const void *k, const
         (ring_k && (!aligned(ring_k, 16) || !aligned(ring_v, 16))) || (state && !aligned(state, 16)) ||
         !aligned(workspace, 16))
         return SFA_ERR_INVALID_ARG;
+    const int s_per_query = mode == sfa::kQueryHead, running_mean = mode == sfa::kRunningMean;
     const int Hs = s_per_query ? Hq : Hkv;
-    if (workspace_bytes < sfa::prefill_workspace_bytes(B, n, Hs, d)) return SFA_ERR_INVALID_ARG;
+    if (workspace_bytes < sfa::prefill_workspace_bytes(B, n, running_mean ? 3 * Hkv : Hs, d))
+        return SFA_ERR_INVALID_ARG;
 
     sfa::PrefillArgs a;
     a.q = q; a.k = k; a.v = v;
@@ -76,15 +79,23 @@ int prefill_impl(int parts, int s_per_query, const void *q, const void *k, const
     a.out_bf16 = out_dtype == SFA_BF16;
     a.Hs = Hs;
     a.s_per_query = s_per_query;
+    a.running_mean = running_mean;
     const size_t per = (size_t)B * Hs * a.ntiles * d;
     float *ws = static_cast<float *>(workspace);
     a.agg16 = ws;
     a.agg64 = ws + 4 * per;
     a.carry = ws + 5 * per;
+    a.csum16 = a.csum64 = a.ccarry = a.beta64 = nullptr;
+    if (running_mean) {
+        a.csum16 = ws + 6 * per;
+        a.csum64 = ws + 10 * per;
+        a.ccarry = ws + 11 * per;
+        a.beta64 = ws + 12 * per;  // B*Hkv*ntiles floats
+    }
     return hip_status(sfa::launch_prefill(a, static_cast<hipStream_t>(stream), parts));
 }
 
-int decode_impl(int s_per_query, const void *q, const void *k_new, const void *v_new, void *ring_k,
+int decode_impl(int mode, const void *q, const void *k_new, const void *v_new, void *ring_k,
                 void *ring_v, float *state, const int32_t *pos, const float *gamma, const float *alpha,
                 void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale, int in_dtype,
                 int out_dtype, void *stream) {
@@ -109,7 +120,8 @@ int decode_impl(int s_per_query, const void *q, const void *k_new, const void *v
     a.scale_log2e = scale_log2e(scale, d);
     a.in_bf16 = in_dtype == SFA_BF16;
     a.out_bf16 = out_dtype == SFA_BF16;
-    a.s_per_query = s_per_query;
+    a.s_per_query = mode == sfa::kQueryHead;
+    a.running_mean = mode == sfa::kRunningMean;
     return hip_status(sfa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -119,9 +131,9 @@ int sfa_prefill(const void *q, const void *k, const void *v, const float *gamma,
                 void *out, void *ring_k, void *ring_v, float *state, const int32_t *pos0, int B,
                 int n, int Hq, int Hkv, int d, int window, float scale, int in_dtype, int out_dtype,
                 void *workspace, size_t workspace_bytes, void *stream) {
-    return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, 0, q, k, v, gamma, alpha, out, ring_k,
-                        ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype, out_dtype,
-                        workspace, workspace_bytes, stream);
+    return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, sfa::kKvHead, q, k, v, gamma, alpha, out,
+                        ring_k, ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype,
+                        out_dtype, workspace, workspace_bytes, stream);
 }
 
 int sfa_prefill_part(int parts, const void *q, const void *k, const void *v, const float *gamma,
@@ -129,33 +141,51 @@ int sfa_prefill_part(int parts, const void *q, const void *k, const void *v, con
                      const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
                      float scale, int in_dtype, int out_dtype, void *workspace,
                      size_t workspace_bytes, void *stream) {
-    return prefill_impl(parts, 0, q, k, v, gamma, alpha, out, ring_k, ring_v, state, pos0, B, n, Hq,
-                        Hkv, d, window, scale, in_dtype, out_dtype, workspace, workspace_bytes, stream);
+    return prefill_impl(parts, sfa::kKvHead, q, k, v, gamma, alpha, out, ring_k, ring_v, state, pos0, B,
+                        n, Hq, Hkv, d, window, scale, in_dtype, out_dtype, workspace, workspace_bytes,
+                        stream);
 }
 
 int sfa_prefill_qh(const void *q, const void *k, const void *v, const float *gamma, const float *alpha,
                    void *out, void *ring_k, void *ring_v, float *state, const int32_t *pos0, int B,
                    int n, int Hq, int Hkv, int d, int window, float scale, int in_dtype,
                    int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
-    return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, 1, q, k, v, gamma, alpha, out, ring_k,
-                        ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype, out_dtype,
-                        workspace, workspace_bytes, stream);
+    return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, sfa::kQueryHead, q, k, v, gamma, alpha,
+                        out, ring_k, ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype,
+                        out_dtype, workspace, workspace_bytes, stream);
+}
+
+int sfa_prefill_rm(const void *q, const void *k, const void *v, const float *gamma, const float *alpha,
+                   void *out, void *ring_k, void *ring_v, float *state, const int32_t *pos0, int B,
+                   int n, int Hq, int Hkv, int d, int window, float scale, int in_dtype,
+                   int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, sfa::kRunningMean, q, k, v, gamma, alpha,
+                        out, ring_k, ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype,
+                        out_dtype, workspace, workspace_bytes, stream);
 }
 
 int sfa_decode_step(const void *q, const void *k_new, const void *v_new, void *ring_k, void *ring_v,
                     float *state, const int32_t *pos, const float *gamma, const float *alpha,
                     void *out, int L, int B, int Hq, int Hkv, int d, int window, float scale,
                     int in_dtype, int out_dtype, void *stream) {
-    return decode_impl(0, q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, out, L, B, Hq,
-                       Hkv, d, window, scale, in_dtype, out_dtype, stream);
+    return decode_impl(sfa::kKvHead, q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, out, L,
+                       B, Hq, Hkv, d, window, scale, in_dtype, out_dtype, stream);
 }
 
 int sfa_decode_step_qh(const void *q, const void *k_new, const void *v_new, void *ring_k,
                        void *ring_v, float *state, const int32_t *pos, const float *gamma,
                        const float *alpha, void *out, int L, int B, int Hq, int Hkv, int d,
                        int window, float scale, int in_dtype, int out_dtype, void *stream) {
-    return decode_impl(1, q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, out, L, B, Hq,
-                       Hkv, d, window, scale, in_dtype, out_dtype, stream);
+    return decode_impl(sfa::kQueryHead, q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, out,
+                       L, B, Hq, Hkv, d, window, scale, in_dtype, out_dtype, stream);
+}
+
+int sfa_decode_step_rm(const void *q, const void *k_new, const void *v_new, void *ring_k,
+                       void *ring_v, float *state, const int32_t *pos, const float *gamma,
+                       const float *alpha, void *out, int L, int B, int Hq, int Hkv, int d,
+                       int window, float scale, int in_dtype, int out_dtype, void *stream) {
+    return decode_impl(sfa::kRunningMean, q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha,
+                       out, L, B, Hq, Hkv, d, window, scale, in_dtype, out_dtype, stream);
 }
 
 size_t sfa_enhance_workspace_size(int L, int T, int H) {

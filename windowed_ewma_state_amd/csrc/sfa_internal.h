@@ -8,6 +8,11 @@
 
 namespace sfa {
 
+// far-field variants of the prefill and decode kernels
+constexpr int kKvHead = 0;       // S and γ per KV head, one evicted key per step (the main reading)
+constexpr int kQueryHead = 1;    // S and γ per query head
+constexpr int kRunningMean = 2;  // per KV head; EWMA input = mean of every key that has left the window
+
 struct DecodeArgs {
     const void *q, *k_new, *v_new;
     void *ring_k, *ring_v;
@@ -18,7 +23,8 @@ struct DecodeArgs {
     int L, B, Hq, Hkv, d, W, group;
     float scale_log2e;
     int in_bf16, out_bf16;
-    int s_per_query;  // S and γ per query head ([L,B,Hq,d], [L,Hq]) instead of per KV head
+    int s_per_query;   // S and γ per query head ([L,B,Hq,d], [L,Hq]) instead of per KV head
+    int running_mean;  // state [L,B,Hkv,2,d]: S, then the mean of the keys that have left the window
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
@@ -39,10 +45,17 @@ struct PrefillArgs {
     // far-field heads: Hs = Hkv (S and γ per KV head) or Hq (per query head,
     // s_per_query = 1); the scan runs over B*Hs chains
     int Hs, s_per_query;
+    // running mean (state [B,Hkv,2,d]): the EWMA input at p >= W is C/m, C the
+    // sum of the m = p-W+1 keys that have left the window
+    int running_mean;
     // workspace carve-up (fp32)
     float *agg16;  // [B*Hs][ntiles][4][d]  local EWMA aggregate of each 16-token block
     float *agg64;  // [B*Hs][ntiles][d]     local EWMA aggregate of each 64-token tile
     float *carry;  // [B*Hs][ntiles][d]     S just before each tile
+    // running mean only: the same for the key sum C, and per tile the
+    // coefficient of the incoming C in the tile's outgoing S
+    float *csum16, *csum64, *ccarry;  // as agg16, agg64, carry
+    float *beta64;                    // [B*Hs][ntiles]
 };
 size_t prefill_workspace_bytes(int B, int n, int Hkv, int d);
 constexpr int kPrefillScan = 1, kPrefillAttend = 2;

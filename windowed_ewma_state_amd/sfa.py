@@ -64,7 +64,8 @@ def prefill_workspace_size(B: int, n: int, Hkv: int, d: int) -> int:
 
 def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=None,
             out_dtype=None, ring_k=None, ring_v=None, state=None, pos0=None, workspace=None,
-            stream=None, parts: int | None = None, gamma_per_query_head: bool = False):
+            stream=None, parts: int | None = None, gamma_per_query_head: bool = False,
+            running_mean: bool = False):
     """sfa_prefill: q [B,n,Hq,d], k/v [B,n,Hkv,d] (BNHD, bf16 or fp32).
 
     gamma: [Hkv] (or scalar) decay per KV head; alpha: [Hq] (or scalar).
@@ -73,13 +74,18 @@ def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=
     int32) to continue an existing cache.  `parts` (SFA_PREFILL_SCAN = 1,
     SFA_PREFILL_ATTEND = 2) selects sfa_prefill_part; the two parts must share
     every argument, including the workspace.  gamma_per_query_head=True calls
-    sfa_prefill_qh: gamma [Hq] and state [B,Hq,d].
+    sfa_prefill_qh: gamma [Hq] and state [B,Hq,d].  running_mean=True calls
+    sfa_prefill_rm: state [B,Hkv,2,d] (S, then the mean of the keys that have
+    left the window).
     """
     B, n, Hq, d = q.shape
     Hkv = k.shape[2]
-    if gamma_per_query_head and parts is not None:
-        raise ValueError("sfa_prefill_qh runs both parts")
+    if (gamma_per_query_head or running_mean) and parts is not None:
+        raise ValueError("sfa_prefill_qh / sfa_prefill_rm run both parts")
+    if gamma_per_query_head and running_mean:
+        raise ValueError("gamma_per_query_head and running_mean are separate entry points")
     Hs = Hq if gamma_per_query_head else Hkv
+    sshape = (B, Hkv, 2, d) if running_mean else (B, Hs, d)
     dev = q.device
     W = int(window)
     in_code = _dtype_code(q, "q")
@@ -91,15 +97,17 @@ def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=
         ring_k = torch.zeros((B, Hkv, W, d), dtype=q.dtype, device=dev)
         ring_v = torch.zeros((B, Hkv, W, d), dtype=q.dtype, device=dev)
     if state is None and pos0 is None:
-        state = torch.zeros((B, Hs, d), dtype=torch.float32, device=dev)
+        state = torch.zeros(sshape, dtype=torch.float32, device=dev)
     g = _vec(gamma, Hs, dev, "gamma")
     a = _vec(alpha, Hq, dev, "alpha")
-    need = prefill_workspace_size(B, n, Hs, d)
+    need = prefill_workspace_size(B, n, 3 * Hkv if running_mean else Hs, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     L = _lib.lib()
     if gamma_per_query_head:
         fn = L.sfa_prefill_qh
+    elif running_mean:
+        fn = L.sfa_prefill_rm
     else:
         fn = L.sfa_prefill if parts is None else (lambda *a_: L.sfa_prefill_part(int(parts), *a_))
     st = fn(
@@ -108,26 +116,31 @@ def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=
         _dev(out, "out", None, (B, n, Hq, d), dev),
         _dev(ring_k, "ring_k", q.dtype, (B, Hkv, W, d), dev),
         _dev(ring_v, "ring_v", q.dtype, (B, Hkv, W, d), dev),
-        _dev(state, "state", torch.float32, (B, Hs, d), dev),
+        _dev(state, "state", torch.float32, sshape, dev),
         _dev(pos0, "pos0", torch.int32, (B,), dev),
         B, n, Hq, Hkv, d, W, float(scale), in_code, out_code,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream, dev))
-    _lib.check(st, "sfa_prefill_qh" if gamma_per_query_head else
+    _lib.check(st, "sfa_prefill_qh" if gamma_per_query_head else "sfa_prefill_rm" if running_mean else
                "sfa_prefill" if parts is None else "sfa_prefill_part")
     return out, ring_k, ring_v, state
 
 
 def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, *, scale: float = 0.0,
-                out=None, out_dtype=None, stream=None, gamma_per_query_head: bool = False):
+                out=None, out_dtype=None, stream=None, gamma_per_query_head: bool = False,
+                running_mean: bool = False):
     """sfa_decode_step over L layers: q [L,B,Hq,d], k_new/v_new [L,B,Hkv,d],
     ring_k/ring_v [L,B,Hkv,W,d] and state [L,B,Hkv,d] fp32 updated in place,
     pos [B] int32, gamma [L,Hkv], alpha [L,Hq].  Returns out [L,B,Hq,d].
     gamma_per_query_head=True calls sfa_decode_step_qh: gamma [L,Hq] and
-    state [L,B,Hq,d]."""
+    state [L,B,Hq,d].  running_mean=True calls sfa_decode_step_rm: state
+    [L,B,Hkv,2,d]."""
     L, B, Hq, d = q.shape
     Hkv = k_new.shape[2]
+    if gamma_per_query_head and running_mean:
+        raise ValueError("gamma_per_query_head and running_mean are separate entry points")
     Hs = Hq if gamma_per_query_head else Hkv
+    sshape = (L, B, Hkv, 2, d) if running_mean else (L, B, Hs, d)
     W = ring_k.shape[3]
     dev = q.device
     in_code = _dtype_code(q, "q")
@@ -137,17 +150,19 @@ def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, *, sc
     out_code = _dtype_code(out, "out")
     g = _vec(gamma, L * Hs, dev, "gamma")
     a = _vec(alpha, L * Hq, dev, "alpha")
-    fn = _lib.lib().sfa_decode_step_qh if gamma_per_query_head else _lib.lib().sfa_decode_step
+    name = ("sfa_decode_step_qh" if gamma_per_query_head else "sfa_decode_step_rm" if running_mean
+            else "sfa_decode_step")
+    fn = getattr(_lib.lib(), name)
     st = fn(
         _dev(q, "q", q.dtype, (L, B, Hq, d), dev), _dev(k_new, "k_new", q.dtype, (L, B, Hkv, d), dev),
         _dev(v_new, "v_new", q.dtype, (L, B, Hkv, d), dev),
         _dev(ring_k, "ring_k", q.dtype, (L, B, Hkv, W, d), dev),
         _dev(ring_v, "ring_v", q.dtype, (L, B, Hkv, W, d), dev),
-        _dev(state, "state", torch.float32, (L, B, Hs, d), dev),
+        _dev(state, "state", torch.float32, sshape, dev),
         _dev(pos, "pos", torch.int32, (B,), dev), _dev(g, "gamma"), _dev(a, "alpha"),
         _dev(out, "out", None, (L, B, Hq, d), dev),
         L, B, Hq, Hkv, d, W, float(scale), in_code, out_code, _stream(stream, dev))
-    _lib.check(st, "sfa_decode_step_qh" if gamma_per_query_head else "sfa_decode_step")
+    _lib.check(st, name)
     return out
 
 

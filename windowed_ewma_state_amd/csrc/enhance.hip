@@ -13,18 +13,16 @@
 //
 // Launches:
 //   k_pool_prep    pool -> bf16 hi/lo in the two MFMA operand orders.
-//   k_slot_norm    |s| of every pool slot.
+//   k_slot_norm    1/|s| of every pool slot; the band/field and identity operands.
 //   k_field_agg    EMA of each 64-token tile from zero (a thread per 16-byte column chunk).
 //   k_field_carry  field before each tile (exclusive scan), final field.
-//   k_enhance      one workgroup per (layer, 64-token tile), XCD-aware order;
-//                  wave w owns a quarter of the hidden dimension:
-//                    cosine scores  C^T = pool · a^T over its quarter (MFMA,
-//                                   each pool operand reused by 4 token
-//                                   groups of 16), partials summed via LDS,
-//                    softmax over the 64 slots (wave w: token group w),
-//                    per 64-column chunk of its quarter and 16-token group:
-//                    ring-mean + field scan into LDS, semantic sum
-//                    sem^T = pool^T · w^T (MFMA), clip, scale, add, store.
+//   k_sem          one workgroup per (layer, 64-token tile): cosine scores
+//                  C^T = pool · a^T (MFMA), softmax over the slots, 0.5·weights
+//                  as MFMA operands in the workspace.
+//   k_cols         one workgroup per (layer, 64-token tile, 128 columns): the
+//                  tile staged column-major in LDS; ring mean, field and the
+//                  semantic sum as one MFMA contraction per 16-token group,
+//                  clip, scale, add, store.
 //   k_ring_out     last min(R, T) attention rows -> ring (after all reads).
 // Precision: the fp32 pool and the softmax weights enter the MFMAs as bf16
 // hi + lo pairs (x = hi + lo to ~2^-17 relative); bf16 attention values are
@@ -97,7 +95,10 @@ __global__ __launch_bounds__(256) void k_pool_prep(EnhanceArgs a) {
     }
     if (j < 2) {  // semantic operand for the two 16-column tiles of this step
         const int xg = 2 * ks + j;
-        const int x = 16 * xg + c16;
+        // row m of half h of the 32-column pair p = xg/2 is column
+        // 32p + 8(m/4) + 4h + m%4: after both halves a lane of the MFMA output
+        // holds 8 consecutive columns
+        const int x = 32 * (xg >> 1) + 8 * (c16 >> 2) + 4 * (xg & 1) + (c16 & 3);
 #pragma unroll
         for (int sk = 0; sk < 2; ++sk) {
             float v[8];
@@ -199,7 +200,12 @@ __global__ __launch_bounds__(256) void k_field_carry(EnhanceArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_enhance
+// k_sem: one workgroup per (layer, 64-token tile), XCD-aware order.  Wave w
+// first scores a quarter of the hidden dimension for all 64 tokens (cosine
+// numerators C^T = pool · a^T on MFMA, each pool operand reused by the four
+// 16-token groups), the partials meet in LDS, then wave w takes token group w
+// through the softmax over the slots and writes 0.5·w as the bf16 hi/lo B
+// operands of the semantic sum.
 // ---------------------------------------------------------------------------
 // eight attention values (raw 16-byte words) -> bf16 hi (+ lo for fp32) and Σa²
 template <typename TIn>
@@ -227,72 +233,29 @@ __device__ __forceinline__ void split_a8<float>(const u32x4 *w, bf16x8 &hi, bf16
     }
 }
 
-template <typename T>
-__device__ __forceinline__ f32x4 load4f(const T *p);
-template <>
-__device__ __forceinline__ f32x4 load4f<float>(const float *p) {
-    const float4 v = *reinterpret_cast<const float4 *>(p);
-    return f32x4{v.x, v.y, v.z, v.w};
-}
-template <>
-__device__ __forceinline__ f32x4 load4f<__bf16>(const __bf16 *p) {
-    const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
-    return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-}
-
-template <typename TOut>
-__device__ __forceinline__ void store4o(TOut *p, f32x4 v);
-template <>
-__device__ __forceinline__ void store4o<float>(float *p, f32x4 v) {
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-template <>
-__device__ __forceinline__ void store4o<__bf16>(__bf16 *p, f32x4 v) {
-    u32x2 w;
-    w[0] = pack_bf16x2(v[0], v[1]);
-    w[1] = pack_bf16x2(v[2], v[3]);
-    *reinterpret_cast<u32x2 *>(p) = w;
-}
-
-template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
+template <typename TIn>
+__global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
     constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split a as well
-    constexpr int XS = kCols + 4;                                // LDS row stride (floats)
-    // phase 4 stages a quarter of the tile's columns (256) for tokens tb-16 ..
-    // tb+63 in LDS, aliasing the phase 1 exchange (cosine partials)
-    constexpr int kRowsE = kBlk + kTile;          // staged rows: tokens tb-16 .. tb+63
-    constexpr int kQCols = 4 * kCols;             // columns per quarter, one 64-column chunk per wave
-    constexpr int EPC = 16 / sizeof(TIn);         // elements per 16-byte piece
-    constexpr int QCH = kQCols / EPC;             // 16-byte pieces per staged row
-    constexpr int AS = kQCols + EPC;              // staged row stride (elements)
-    constexpr int NST = kRowsE * QCH / 256;       // staging loads per thread
-    static_assert(kRowsE * QCH % 256 == 0, "staging must split evenly over the workgroup");
     struct Phase1 {
         f32x4 cp[4][2][4][64];  // [wave][slot tile in round][token group][lane]
         float sq[4][4][64];     // [wave][token group][lane]
     };
-    constexpr int kStageBytes = kRowsE * AS * (int)sizeof(TIn);
-    __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(Phase1) > kStageBytes
-                                                               ? sizeof(Phase1) : kStageBytes];
-    __shared__ __attribute__((aligned(16))) float Xs[4][kBlk * XS];  // per wave: ring mean/R + 0.5·field
-    __shared__ __attribute__((aligned(16))) u32x4 Wx[4][2][2][64];  // [tg][ks][hi/lo][lane]
-    Phase1 &p1 = *reinterpret_cast<Phase1 *>(smem);
-    TIn *Ast = reinterpret_cast<TIn *>(smem);
+    __shared__ __attribute__((aligned(16))) Phase1 p1;
 
     const int lid = xcd_remap(blockIdx.x, a.L * a.ntiles);
     const int l = lid / a.ntiles, tile = lid % a.ntiles;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q4 = lane >> 4, c16 = lane & 15;
-    const int H = a.H, T = a.T, R = a.R;
+    const int H = a.H, T = a.T;
     const int tb = tile * kTile;
     const int pl = a.pool_stride == 0 ? 0 : l;
     const int ksteps = H / 32;
     const uint16_t *poolA = a.poolA + (long)pl * ksteps * 4 * 2 * kOpElems + lane * 8;
-    const uint16_t *poolT = a.poolT + (long)pl * (H / 16) * 2 * 2 * kOpElems + lane * 8;
-    const float *snorm = a.slot_norm + pl * kSlots;
+    const float *sinv = a.slot_norm + pl * kSlots;  // 1 / |s| per slot
     const TIn *Ag = reinterpret_cast<const TIn *>(a.attn) + (long)l * T * H;
-    const float al = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
     const int nj = (a.n_slots + 15) / 16;
+    // B operands of this wave's token group, [ks][hi/lo][lane][8]
+    uint16_t *wsem = a.wsem + (((long)l * a.ntiles + tile) * 4 + wave) * 4 * kOpElems + lane * 8;
 
     // ---- (1) partial cosine scores over this wave's quarter of the hidden dim ----
     // lane holds C^T[slot 16j+4q4+i][token tb+16tg+c16] for its k-steps
@@ -366,28 +329,10 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
             compute_ops(o1);
         }
     }
-    // the first column quarter's staging loads fly during phases 2 and 3
-    u32x4 stg[NST];
-    auto stage_load = [&](int q) {
+    // the reciprocal norms of this lane's 16 slots go out before the exchange
+    float isn[16];
 #pragma unroll
-        for (int k = 0; k < NST; ++k) {
-            const int idx = threadIdx.x + 256 * k;
-            const int r = idx / QCH, c = idx % QCH;
-            const int t = tb - kBlk + r;
-            const int col = q * kQCols + c * EPC;
-            stg[k] = u32x4{0u, 0u, 0u, 0u};
-            if (t >= 0 && t < T && col < H) stg[k] = *reinterpret_cast<const u32x4 *>(Ag + (long)t * H + col);
-        }
-    };
-    auto stage_store = [&]() {
-#pragma unroll
-        for (int k = 0; k < NST; ++k) {
-            const int idx = threadIdx.x + 256 * k;
-            const int r = idx / QCH, c = idx % QCH;
-            *reinterpret_cast<u32x4 *>(&Ast[r * AS + c * EPC]) = stg[k];
-        }
-    };
-    stage_load(0);
+    for (int k = 0; k < 16; ++k) isn[k] = sinv[16 * (k >> 2) + 4 * q4 + (k & 3)];
 
     // ---- (2) reduce the four partials: wave w ends with token group tg = w -------
     f32x4 Cw[4];
@@ -424,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int slot = 16 * j + 4 * q4 + i;
-                w[4 * j + i] = slot < a.n_slots ? Cw[j][i] * inv_na / snorm[slot] * a.inv_temp_log2e
+                w[4 * j + i] = slot < a.n_slots ? Cw[j][i] * inv_na * isn[4 * j + i] * a.inv_temp_log2e
                                                 : -INFINITY;
                 m = fmaxf(m, w[4 * j + i]);
             }
@@ -443,166 +388,309 @@ __global__ __launch_bounds__(256, 2) void k_enhance(EnhanceArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 __bf16 h, lo_;
-                split_bf16(w[4 * (2 * ks + (e >> 2)) + (e & 3)] * inv, h, lo_);
+                split_bf16(0.5f * w[4 * (2 * ks + (e >> 2)) + (e & 3)] * inv, h, lo_);  // 0.5·semantic
                 h8[e] = h;
                 l8[e] = lo_;
             }
-            Wx[wave][ks][0][lane] = __builtin_bit_cast(u32x4, h8);
-            Wx[wave][ks][1][lane] = __builtin_bit_cast(u32x4, l8);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(wsem + (ks * 2) * kOpElems);
+            dst[0] = __builtin_bit_cast(u32x4, h8);
+            dst[kOpElems / 8] = __builtin_bit_cast(u32x4, l8);
         }
     }
-    __syncthreads();
+}
 
-    // ---- (4) column quarters: stage, then each wave scans its 64-column chunk ----
-    // from LDS (ring mean and field along the tokens), and per 16-token group
-    // does the semantic sum (MFMA) and the epilogue
-    const float g = a.ema_gamma;
-    const float invR = 1.f / (float)R;
+// ---------------------------------------------------------------------------
+// k_cols: one workgroup per (layer, 64-token tile, 128-column block); wave w
+// owns the 32 columns 32w .. 32w+31 of the block.  The block's attention
+// values for tokens tb-16 .. tb+63 are staged in LDS column by column (tokens
+// contiguous), so one 16-byte read hands a lane its MFMA operand of eight
+// consecutive tokens.  Per 16-token group one accumulator takes
+//   D[x][t] = Σ_j A[j][x]·Coef[t][j] + Σ_s pool[s][x]·0.5·w[t][s],
+//   Coef[t][j] = 1/R on the ring band (tokens t-R+1 .. t)
+//              + 0.5(1-γ)γ^(t-j) for the tile's tokens j <= t,
+// and a second one passes a itself through (an identity operand, exact for
+// bf16 values); then
+//   e = D + 0.5·γ^(t+1)·(field before the tile)
+//         [+ the carried ring's share of the band in the call's first tile],
+//   out = a + α_l·clip(e).
+// Every load is issued before the first output store (outputs wait in
+// registers until the end), so no wait for a load ever waits for a store.
+// ---------------------------------------------------------------------------
+constexpr int kCB = 128;       // columns per workgroup
+constexpr int kCoefEnt = 8;    // (token group, k-step) pairs of the band/field operand
+constexpr int kTabEntries = (kCoefEnt * 2 + 4) * 64;  // coefficient + identity operands (u32x4)
+// token group tg uses the k-steps s = 0 .. kSteps[tg]-1 (staged rows 32s .. 32s+31),
+// table entries {0, 1, 3, 5}[tg] + s; its own tokens sit in k-step kIdStep[tg]
+
+template <typename TIn>
+struct ColLayout;
+template <>
+struct ColLayout<__bf16> {
+    // column c: chunk b (staged tokens 8b .. 8b+7, 16 bytes) at 16·(b ^ ((c >> 3) & 3))
+    static constexpr int kColBytes = 192;
+    __device__ static int chunk(int c, int b) { return c * kColBytes + 16 * (b ^ ((c >> 3) & 3)); }
+};
+template <>
+struct ColLayout<float> {
+    // column c: chunk b (staged tokens 4b .. 4b+3, 16 bytes) at 16·b
+    static constexpr int kColBytes = 336;
+    __device__ static int chunk(int c, int b) { return c * kColBytes + 16 * b; }
+};
+
+// value of the band/field operand: token t of the tile, staged row j (token j-16)
+__device__ __forceinline__ float band_field_coef(int t, int j, int R, float g) {
+    const int tj = j - kBlk;
+    float c = (tj >= t - R + 1 && tj <= t && j < kBlk + kTile) ? 1.f / (float)R : 0.f;
+    if (tj >= 0 && tj <= t) c += 0.5f * (1.f - g) * powi(g, t - tj);
+    return c;
+}
+
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
+    constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split a
+    using LY = ColLayout<TIn>;
+    constexpr int kRowsE = kBlk + kTile;     // staged tokens tb-16 .. tb+63
+    constexpr int EPC = 16 / sizeof(TIn);    // columns per 16-byte piece
+    constexpr int CPR = kCB / EPC;           // pieces per staged row
+    constexpr int NITEM = kRowsE / 4 * CPR;  // staging items: 4 tokens x one piece
+    constexpr int NIT = (NITEM + 255) / 256;
+    static_assert(NITEM % 64 == 0, "a partial item round must cover whole waves");
+    constexpr int NTAB = (kPrecise ? kCoefEnt * 2 : kCoefEnt * 2 + 4) * 64;
+    static_assert(NTAB % 256 == 0, "table copy must split evenly");
+    constexpr int kSteps[4] = {1, 2, 2, 3}, kIdStep[4] = {0, 1, 1, 2};
+    constexpr int OW = 2 * (int)sizeof(TOut);  // output dwords per 8 values
+    __shared__ __attribute__((aligned(16))) unsigned char AsT[kCB * LY::kColBytes];
+    __shared__ __attribute__((aligned(16))) u32x4 TabS[NTAB];
+
+    const int ncb = (a.H + kCB - 1) / kCB;
+    const int lid = xcd_remap(blockIdx.x, a.L * a.ntiles * ncb);
+    const int cb = lid % ncb, lt = lid / ncb;  // lt = layer * ntiles + tile
+    const int l = lt / a.ntiles, tile = lt % a.ntiles;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const int H = a.H, T = a.T, R = a.R;
+    const int tb = tile * kTile;
     const int len = min(kTile, T - tb);
-    const float *ringl = a.ring + (long)l * R * H;
-    const int ring0 = a.t0 % R;   // slot of relative token 0
-    const bool reach_ring = tb < R;  // only the first tile looks back before token 0
-    const float *carry = a.carry + ((long)l * a.ntiles + tile) * H;
-    float *Xw = Xs[wave];
-    TOut *Og = reinterpret_cast<TOut *>(a.out) + (long)l * T * H;
-    float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
-    const int nch = H / kCols;
-    const int nq = (H + kQCols - 1) / kQCols;
+    const int xb = cb * kCB;        // the workgroup's first column
+    const int xw = xb + 32 * wave;  // the wave's first column
+    const bool has = xw < H;        // wave-uniform: H is a multiple of 64
+    const int x0 = xw + 8 * q4;     // this lane's 8 output columns
+    const TIn *Ag = reinterpret_cast<const TIn *>(a.attn) + (long)l * T * H;
 
-    for (int q = 0; q < nq; ++q) {
-        __syncthreads();  // the previous quarter (or phase 1) is done with the LDS
-        stage_store();
-        const int ch = 4 * q + wave;
-        const bool has = ch < nch;  // wave-uniform: a partial last quarter leaves waves idle
-        const int xc = ch * kCols;
-        const int x = xc + lane;
-        const int xq = wave * kCols;  // the chunk's first column within the quarter
-        // the chunk's own global reads go out before the next quarter's staging
-        // loads, so waiting for them never waits for the prefetch: the
-        // semantic-sum A operands (4 column tiles x k-steps x hi/lo, shared by
-        // the four token groups), the field carried into the tile, and in the
-        // first tile the R tokens before it from the carried ring, slot
-        // (t0 + t) mod R for t = -R..-1, parked in rows 16-R..15 of the X tile
-        bf16x8 pt[kCols / 16][4];
-        float F = 0.f;
-        if (has) {
+    // ---- (1) loads: staging items, the operand table, pool^T, field carry ----
+    u32x4 stg[NIT][4];
 #pragma unroll
-            for (int xt = 0; xt < kCols / 16; ++xt)
+    for (int k = 0; k < NIT; ++k) {
+        const int it = threadIdx.x + 256 * k;
+        if (it < NITEM) {  // wave-uniform
+            const int rq = it / CPR, cp = it % CPR;
+            const int col = xb + cp * EPC;
 #pragma unroll
-                for (int o = 0; o < 4; ++o) pt[xt][o] = get8(poolT + ((long)(xc / 16 + xt) * 4 + o) * kOpElems);
-            F = carry[x];
-            if (reach_ring) {
+            for (int i = 0; i < 4; ++i) {
+                const int t = tb - kBlk + 4 * rq + i;
+                stg[k][i] = u32x4{0u, 0u, 0u, 0u};
+                if (t >= 0 && t < T && col < H) stg[k][i] = *reinterpret_cast<const u32x4 *>(Ag + (long)t * H + col);
+            }
+        }
+    }
+    u32x4 tab[NTAB / 256];
 #pragma unroll
-                for (int k = 0; k < kBlk; ++k) {
-                    const int t = k - kBlk;
-                    if (t >= -R) {
-                        const int slot = ring0 + t < 0 ? ring0 + t + R : ring0 + t;
-                        Xw[k * XS + lane] = ringl[(long)slot * H + x];
+    for (int k = 0; k < NTAB / 256; ++k) tab[k] = reinterpret_cast<const u32x4 *>(a.coef)[threadIdx.x + 256 * k];
+    const int pl = a.pool_stride == 0 ? 0 : l;
+    const uint16_t *poolT = a.poolT + (long)pl * (H / 16) * 2 * 2 * kOpElems + lane * 8;
+    bf16x8 pt[2][2][2];  // [half][slot k-step][hi/lo]
+    float Fc[8];
+    if (has) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    pt[h][sk][hl] = get8(poolT + (((long)(xw / 16 + h) * 2 + sk) * 2 + hl) * kOpElems);
+        const float *carry = a.carry + (long)lt * H + x0;
+#pragma unroll
+        for (int k = 0; k < 8; k += 4) {
+            const float4 c4 = *reinterpret_cast<const float4 *>(carry + k);
+            Fc[k] = c4.x; Fc[k + 1] = c4.y; Fc[k + 2] = c4.z; Fc[k + 3] = c4.w;
+        }
+    }
+    // semantic weights of the tile, B operands [tg][ks][hi/lo]: two token groups
+    // ahead, the next pair as each group finishes with its own
+    const uint16_t *wsem = a.wsem + (long)lt * 4 * 4 * kOpElems + lane * 8;
+    bf16x8 wb[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int o = 0; o < 4; ++o) wb[b][o] = get8(wsem + (b * 4 + o) * kOpElems);
+
+    // ---- (2) staging -> column-major LDS tile; table -> LDS ------------------
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int it = threadIdx.x + 256 * k;
+        if (it < NITEM) {
+            const int rq = it / CPR, cp = it % CPR;
+            if constexpr (!kPrecise) {
+                // 4 tokens x 8 columns: per column the 4 tokens as one 8-byte write
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int wd = e >> 1;
+                    u32x2 v;
+                    if (e & 1) {
+                        v[0] = (stg[k][0][wd] >> 16) | (stg[k][1][wd] & 0xffff0000u);
+                        v[1] = (stg[k][2][wd] >> 16) | (stg[k][3][wd] & 0xffff0000u);
+                    } else {
+                        v[0] = (stg[k][0][wd] & 0xffffu) | (stg[k][1][wd] << 16);
+                        v[1] = (stg[k][2][wd] & 0xffffu) | (stg[k][3][wd] << 16);
                     }
-                }
-            }
-        }
-        if (q + 1 < nq) stage_load(q + 1);
-        __syncthreads();
-        if (!has) continue;
-        // value of relative token t (-16 <= t < 64) at column x: staged rows, or
-        // for t < 0 in the first tile the parked ring values
-        const TIn *Acol = Ast + xq + lane;
-        auto before = [&](int t) -> float {  // t < 0
-            const float xa = Xw[max(0, kBlk + t) * XS + lane];
-            const float sa = (float)Acol[(kBlk + t) * AS];
-            return reach_ring ? xa : sa;
-        };
-        // ring mean of tokens -R .. -1 (kept pre-divided by R), then slide:
-        // + token t, - token t-R; the field is kept pre-halved (F' = F / 2)
-        float rs = 0.f;
-#pragma unroll
-        for (int k = 0; k < kBlk; ++k) {
-            const float v = before(-1 - k);
-            rs += k < R ? v : 0.f;
-        }
-        rs *= invR;
-        F *= 0.5f;
-        const float hg = 0.5f * (1.f - g);
-        for (int tg = 0; tg < 4; ++tg) {
-            const int j0 = 16 * tg;
-            if (j0 >= len) break;  // wave-uniform
-            // the group's 32 reads go out together; the first group takes the
-            // tokens before the tile where t - R < 0
-            float cur[kBlk], old[kBlk];
-#pragma unroll
-            for (int j = 0; j < kBlk; ++j) {
-                const int t = j0 + j;
-                cur[j] = (float)Acol[(kBlk + t) * AS];
-                const float os = (float)Acol[(kBlk + t - R) * AS];
-                old[j] = (tg == 0 && t - R < 0) ? before(t - R) : os;
-            }
-            if (j0 + kBlk <= len) {  // wave-uniform: a whole group of tokens
-#pragma unroll
-                for (int j = 0; j < kBlk; ++j) {
-                    rs = fmaf(cur[j] - old[j], invR, rs);
-                    F = fmaf(g, F, hg * cur[j]);
-                    Xw[j * XS + lane] = rs + F;
+                    *reinterpret_cast<u32x2 *>(AsT + LY::chunk(cp * 8 + e, rq >> 1) + 8 * (rq & 1)) = v;
                 }
             } else {
+                // 4 tokens x 4 columns: per column one 16-byte write
 #pragma unroll
-                for (int j = 0; j < kBlk; ++j) {
-                    const bool ok = j0 + j < len;
-                    rs = ok ? fmaf(cur[j] - old[j], invR, rs) : rs;
-                    F = ok ? fmaf(g, F, hg * cur[j]) : F;
-                    Xw[j * XS + lane] = rs + F;
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<u32x4 *>(AsT + LY::chunk(cp * 4 + e, rq)) =
+                        u32x4{stg[k][0][e], stg[k][1][e], stg[k][2][e], stg[k][3][e]};
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NTAB / 256; ++k) TabS[threadIdx.x + 256 * k] = tab[k];
+    __syncthreads();
+    if (!has) return;  // no barrier follows
+
+    // ---- (3) A operands: the staged values, row m of half h = column 8(m/4) + 4h + m%4
+    bf16x8 Av[3][2], Al[kPrecise ? 3 : 1][2];
+#pragma unroll
+    for (int st = 0; st < 3; ++st)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = 32 * wave + 8 * (c16 >> 2) + 4 * h + (c16 & 3);
+            int b = 4 * st + q4;  // 8-token chunk; past the 80 staged tokens read 16 earlier
+            if (b >= kRowsE / 8) b -= 2;  // (their coefficients are zero)
+            if constexpr (!kPrecise) {
+                Av[st][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, b)));
+            } else {
+                const u32x4 w0 = *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, 2 * b));
+                const u32x4 w1 = *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, 2 * b + 1));
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = __uint_as_float(w0[e]);
+                    v[4 + e] = __uint_as_float(w1[e]);
+                }
+                uint16_t hi[8], lo[8];
+                split8(v, hi, lo);
+                Av[st][h] = get8(hi);
+                Al[st][h] = get8(lo);
+            }
+        }
+
+    // ---- (4) per token group: contraction, epilogue; outputs held until the end
+    const float g = a.ema_gamma;
+    const float invR = 1.f / (float)R;
+    const float al = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
+    const float gc = powi(g, c16 + 1), g16 = powi(g, kBlk);
+    const float *ringl = a.ring + (long)l * R * H;
+    const int ring0 = a.t0 % R;  // slot of relative token 0
+    float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
+    uint32_t ob[4][OW];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+        if (16 * tg >= len) break;  // wave-uniform
+        const int t = 16 * tg + c16;  // this lane's token (tile-relative)
+        const bf16x8 wh0 = wb[tg & 1][0], wl0 = wb[tg & 1][1], wh1 = wb[tg & 1][2], wl1 = wb[tg & 1][3];
+        f32x4 D[2], Da[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) D[h] = Da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < kSteps[tg]; ++st) {
+            const int ent = (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5) + st;
+            const bf16x8 ch_ = __builtin_bit_cast(bf16x8, TabS[(ent * 2) * 64 + lane]);
+            const bf16x8 cl_ = __builtin_bit_cast(bf16x8, TabS[(ent * 2 + 1) * 64 + lane]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                D[h] = mfma_bf16_16x16x32(Av[st][h], ch_, D[h]);
+                D[h] = mfma_bf16_16x16x32(Av[st][h], cl_, D[h]);
+                if constexpr (kPrecise) D[h] = mfma_bf16_16x16x32(Al[st][h], ch_, D[h]);
+            }
+        }
+        // 0.5·semantic: pool^T · (0.5 w)^T, both split into bf16 hi + lo
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            D[h] = mfma_bf16_16x16x32(pt[h][0][0], wh0, D[h]);
+            D[h] = mfma_bf16_16x16x32(pt[h][0][0], wl0, D[h]);
+            D[h] = mfma_bf16_16x16x32(pt[h][0][1], wh0, D[h]);
+            D[h] = mfma_bf16_16x16x32(pt[h][1][0], wh1, D[h]);
+            D[h] = mfma_bf16_16x16x32(pt[h][1][0], wl1, D[h]);
+            D[h] = mfma_bf16_16x16x32(pt[h][1][1], wh1, D[h]);
+        }
+        if (tg + 2 < 4) {  // every tile has all four groups' weights
+#pragma unroll
+            for (int o = 0; o < 4; ++o) wb[tg & 1][o] = get8(wsem + ((tg + 2) * 4 + o) * kOpElems);
+        }
+        if constexpr (!kPrecise) {  // a itself through the identity operand
+            const bf16x8 id = __builtin_bit_cast(bf16x8, TabS[(kCoefEnt * 2 + tg) * 64 + lane]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) Da[h] = mfma_bf16_16x16x32(Av[kIdStep[tg]][h], id, Da[h]);
+        }
+        // epilogue for the lane's 8 columns of token t
+        const float cF = 0.5f * gc * powi(g16, tg);
+        float halo[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) halo[k] = 0.f;
+        if (tg == 0 && tile == 0 && t < R - 1) {
+            // the band's tokens before the call: the carried ring, slot (t0 + j) mod R
+            for (int j = t - R + 1; j < 0; ++j) {
+                const int slot = ring0 + j < 0 ? ring0 + j + R : ring0 + j;
+                const float *rr = ringl + (long)slot * H + x0;
+#pragma unroll
+                for (int k = 0; k < 8; k += 4) {
+                    const float4 r4 = *reinterpret_cast<const float4 *>(rr + k);
+                    halo[k] += r4.x; halo[k + 1] += r4.y; halo[k + 2] += r4.z; halo[k + 3] += r4.w;
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const bf16x8 wh0 = __builtin_bit_cast(bf16x8, Wx[tg][0][0][lane]);
-            const bf16x8 wl0 = __builtin_bit_cast(bf16x8, Wx[tg][0][1][lane]);
-            const bf16x8 wh1 = __builtin_bit_cast(bf16x8, Wx[tg][1][0][lane]);
-            const bf16x8 wl1 = __builtin_bit_cast(bf16x8, Wx[tg][1][1][lane]);
-            const bool tok_ok_g = tb + j0 + c16 < T;
+        }
+        float o[8], en[8];
 #pragma unroll
-            for (int xt = 0; xt < kCols / 16; ++xt) {
-                const bf16x8 th0 = pt[xt][0], tl0 = pt[xt][1], th1 = pt[xt][2], tl1 = pt[xt][3];
-                f32x4 sm = {0.f, 0.f, 0.f, 0.f};
-                sm = mfma_bf16_16x16x32(th0, wh0, sm);
-                sm = mfma_bf16_16x16x32(th0, wl0, sm);
-                sm = mfma_bf16_16x16x32(tl0, wh0, sm);
-                sm = mfma_bf16_16x16x32(th1, wh1, sm);
-                sm = mfma_bf16_16x16x32(th1, wl1, sm);
-                sm = mfma_bf16_16x16x32(tl1, wh1, sm);
-                // lane: sem[x = xc + 16xt + 4q4 + i][token tb + j0 + c16]
-                const int xl = 16 * xt + 4 * q4;
-                const f32x4 X4 = *reinterpret_cast<const f32x4 *>(&Xw[c16 * XS + xl]);
-                const f32x4 A4 = load4f<TIn>(&Ast[(kBlk + j0 + c16) * AS + xq + xl]);
-                f32x4 o, en;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = fminf(fmaxf(X4[i] + 0.5f * sm[i], -a.clip), a.clip);
-                    en[i] = al * e;
-                    o[i] = A4[i] + en[i];
-                }
-                // the output goes back into the X tile (row c16, same byte row): a
-                // bf16 value lands on fp32 columns [xl/2, xl/2 + 2), which every
-                // lane has read by this column tile, an fp32 value on its own spot
-                store4o<TOut>(reinterpret_cast<TOut *>(&Xw[c16 * XS]) + xl, o);
-                if (Eg && tok_ok_g) store4o<float>(Eg + (long)(tb + j0 + c16) * H + xc + xl, en);
+        for (int k = 0; k < 8; ++k) {
+            const int h = k >> 2, i = k & 3;
+            const float e = fminf(fmaxf(D[h][i] + cF * Fc[k] + halo[k] * invR, -a.clip), a.clip);
+            en[k] = al * e;
+            float av;
+            if constexpr (kPrecise) {
+                const int c = 32 * wave + 8 * q4 + k, r = kBlk + t;
+                av = *reinterpret_cast<const float *>(AsT + LY::chunk(c, r >> 2) + 4 * (r & 3));
+            } else {
+                av = Da[h][i];
             }
-            // whole 128- or 256-byte rows of the 16 x 64 output tile
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            constexpr int OPR = kCols * (int)sizeof(TOut) / 16;  // 16-byte pieces per output row
+            o[k] = av + en[k];
+        }
+        if constexpr (std::is_same<TOut, float>::value) {
 #pragma unroll
-            for (int k = 0; k < kBlk * OPR / 64; ++k) {
-                const int idx = lane + 64 * k;
-                const int r = idx / OPR, c = idx % OPR;
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(
-                    reinterpret_cast<const unsigned char *>(&Xw[r * XS]) + 16 * c);
-                if (j0 + r < len)
-                    st_stream(reinterpret_cast<unsigned char *>(Og + (long)(tb + j0 + r) * H + xc) + 16 * c, w);
-            }
-            __builtin_amdgcn_wave_barrier();
+            for (int k = 0; k < 8; ++k) ob[tg][k] = __float_as_uint(o[k]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ob[tg][i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
+        }
+        if (Eg && tb + t < T) {
+            float *ed = Eg + (long)(tb + t) * H + x0;
+            *reinterpret_cast<float4 *>(ed) = make_float4(en[0], en[1], en[2], en[3]);
+            *reinterpret_cast<float4 *>(ed + 4) = make_float4(en[4], en[5], en[6], en[7]);
+        }
+    }
+    // ---- (5) output rows: 8 consecutive columns per lane -----------------------
+    TOut *Og = reinterpret_cast<TOut *>(a.out) + (long)l * T * H;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+        if (16 * tg >= len) break;
+        const int t = tb + 16 * tg + c16;
+        if (t < T) {
+            TOut *dst = Og + (long)t * H + x0;
+#pragma unroll
+            for (int k = 0; k < OW / 4; ++k)
+                st_stream(reinterpret_cast<unsigned char *>(dst) + 16 * k,
+                          u32x4{ob[tg][4 * k], ob[tg][4 * k + 1], ob[tg][4 * k + 2], ob[tg][4 * k + 3]});
         }
     }
 }
@@ -620,9 +708,40 @@ __global__ __launch_bounds__(256) void k_ring_out(EnhanceArgs a) {
     for (int x = threadIdx.x; x < a.H; x += 256) dst[x] = Elem<TIn>::load(A + x);
 }
 
-// per-slot norms: one workgroup per (pool layer, slot)
+// per-slot reciprocal norms: one workgroup per (pool layer, slot); the workgroups past
+// them write the band/field and identity operands of k_cols (the same for
+// every layer and tile): entry (e, hi/lo) for e = {0, 1, 3, 5}[tg] + s, then
+// the identities of the four token groups
 __global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
     __shared__ float red[4];
+    const int nsn = a.n_pool_layers * kSlots;
+    if ((int)blockIdx.x >= nsn) {
+        const int idx = ((int)blockIdx.x - nsn) * 256 + threadIdx.x;
+        const int ln = idx % 64;
+        float v[8];
+        int hl = 0;
+        if (idx < kCoefEnt * 2 * 64) {
+            const int ent = idx / 128;
+            hl = (idx / 64) & 1;
+            const int tg = ent >= 5 ? 3 : ent >= 3 ? 2 : ent >= 1 ? 1 : 0;
+            const int st = ent - (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = band_field_coef(16 * tg + (ln & 15), 32 * st + 8 * (ln >> 4) + e, a.R, a.ema_gamma);
+        } else {
+            const int tg = (idx - kCoefEnt * 2 * 64) / 64;
+            const int st = tg == 0 ? 0 : tg == 3 ? 2 : 1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (32 * st + 8 * (ln >> 4) + e == kBlk + 16 * tg + (ln & 15)) ? 1.f : 0.f;
+        }
+        uint16_t hi[8], lo[8], pick[8];
+        split8(v, hi, lo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pick[e] = hl ? lo[e] : hi[e];
+        put8(a.coef + (long)idx * 8, pick);
+        return;
+    }
     const int pl = blockIdx.x / kSlots, slot = blockIdx.x % kSlots;
     float ss = 0.f;
     if (slot < a.n_slots) {
@@ -633,18 +752,20 @@ __global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     if (threadIdx.x == 0)
-        a.slot_norm[pl * kSlots + slot] = fmaxf(sqrtf(red[0] + red[1] + red[2] + red[3]), 1e-12f);
+        a.slot_norm[pl * kSlots + slot] = 1.f / fmaxf(sqrtf(red[0] + red[1] + red[2] + red[3]), 1e-12f);
 }
 
 template <typename TIn, typename TOut>
 hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_pool_prep, dim3(a.n_pool_layers * (a.H / 32)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_slot_norm, dim3(a.n_pool_layers * kSlots), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_slot_norm, dim3(a.n_pool_layers * kSlots + kTabEntries / 256), dim3(256), 0, stream, a);
     const int fchunks = a.H / (16 / (int)sizeof(TIn));
     hipLaunchKernelGGL((k_field_agg<TIn>), dim3(a.L * a.ntiles * ((fchunks + 255) / 256)), dim3(256), 0,
                        stream, a);
     hipLaunchKernelGGL(k_field_carry, dim3(a.L * ((a.H + 255) / 256)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((k_enhance<TIn, TOut>), dim3(a.L * a.ntiles), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_sem<TIn>), dim3(a.L * a.ntiles), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_cols<TIn, TOut>), dim3(a.L * a.ntiles * ((a.H + kCB - 1) / kCB)), dim3(256), 0,
+                       stream, a);
     hipLaunchKernelGGL((k_ring_out<TIn>), dim3(a.L * a.R), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
@@ -656,7 +777,10 @@ size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers) {
     const size_t floats = 2 * (size_t)L * nt * H + (size_t)n_pool_layers * kSlots;
     // poolA and poolT: H/32 steps x 4 tiles (resp. H/16 x 2 steps) x hi/lo x 512 bf16
     const size_t ops = (size_t)n_pool_layers * (size_t)H * 64 * 2 * 2;
-    return floats * sizeof(float) + ops * sizeof(uint16_t);
+    // semantic weights: per tile 4 token groups x 2 k-steps x hi/lo x 512 bf16;
+    // the band/field and identity operand table
+    const size_t wsem = (size_t)L * nt * 4 * 4 * kOpElems + (size_t)kTabEntries * 8;
+    return floats * sizeof(float) + (ops + wsem) * sizeof(uint16_t);
 }
 
 hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream) {

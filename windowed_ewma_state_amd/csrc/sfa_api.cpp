@@ -233,6 +233,8 @@ int sfa_enhance(const void *attn, void *out, float *ring, float *field, const fl
     a.slot_norm = ws + 2 * per;
     a.poolA = reinterpret_cast<uint16_t *>(ws + 2 * per + (size_t)n_pool_layers * 64);
     a.poolT = a.poolA + (size_t)n_pool_layers * H * 128;
+    a.wsem = a.poolT + (size_t)n_pool_layers * H * 128;
+    a.coef = a.wsem + (size_t)L * a.ntiles * 4 * 4 * 512;
     return hip_status(sfa::launch_enhance(a, static_cast<hipStream_t>(stream)));
 }
 

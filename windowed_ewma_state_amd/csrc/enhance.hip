@@ -13,12 +13,15 @@
 //
 // Launches:
 //   k_pool_prep    pool -> bf16 hi/lo in the two MFMA operand orders.
-//   k_slot_norm    1/|s| of every pool slot; the band/field and identity operands.
-//   k_field_agg    EMA of each 64-token tile from zero (a thread per 16-byte column chunk).
-//   k_field_carry  field before each tile (exclusive scan), final field.
+//   k_slot_norm    1/|s| of every pool slot; the band/field operands;
+//                  α of each layer.
+//   k_field_agg    EMA of each 64-token tile from zero (a thread per 16-byte
+//                  column chunk); only for hidden sizes above kAggMaxH.
 //   k_sem          one workgroup per (layer, 64-token tile): cosine scores
 //                  C^T = pool · a^T (MFMA), softmax over the slots, 0.5·weights
-//                  as MFMA operands in the workspace.
+//                  as MFMA operands in the workspace; on the same pass over
+//                  the tile, its field aggregate (EMA from zero).
+//   k_field_carry  field before each tile (exclusive scan), final field.
 //   k_cols         one workgroup per (layer, 64-token tile, 128 columns): the
 //                  tile staged column-major in LDS; ring mean, field and the
 //                  semantic sum as one MFMA contraction per 16-token group,
@@ -39,6 +42,16 @@ namespace {
 constexpr int kSlots = 64;
 constexpr int kCols = 64;          // columns per epilogue chunk (one per lane)
 constexpr int kOpElems = 64 * 8;   // one MFMA operand (64 lanes x 8 bf16)
+constexpr int kAggMaxH = 8192;     // hidden sizes whose field aggregate k_sem computes
+
+// sum over the 16 lanes of a DPP row (every lane of the row gets it)
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, true));  // row_ror:8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, true));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, true));  // row_ror:2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, true));  // row_ror:1
+    return v;
+}
 
 __device__ __forceinline__ float alpha_layer(float base, float decay, int layer, int n_layers) {
     const float ratio = n_layers > 1 ? (float)layer / (float)(n_layers - 1) : 0.f;
@@ -241,6 +254,9 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
         float sq[4][4][64];     // [wave][token group][lane]
     };
     __shared__ __attribute__((aligned(16))) Phase1 p1;
+    // during the k-steps the same memory collects the tile's field aggregate
+    static_assert(kAggMaxH * sizeof(float) <= sizeof(Phase1), "aggregate must fit the exchange buffer");
+    float *aggS = reinterpret_cast<float *>(&p1);
 
     const int lid = xcd_remap(blockIdx.x, a.L * a.ntiles);
     const int l = lid / a.ntiles, tile = lid % a.ntiles;
@@ -260,6 +276,17 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
     // ---- (1) partial cosine scores over this wave's quarter of the hidden dim ----
     // lane holds C^T[slot 16j+4q4+i][token tb+16tg+c16] for its k-steps
     const int ks0 = wave * ksteps / 4, ks1 = (wave + 1) * ksteps / 4;
+    const bool fuse_agg = H <= kAggMaxH;
+    float om[4];  // EMA weight of the lane's token in each group: (1-γ)γ^(len-1-t), 0 past the end
+    {
+        const int len = min(kTile, T - tb);
+        const float g = a.ema_gamma;
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) {
+            const int t = 16 * tg + c16;
+            om[tg] = t < len ? (1.f - g) * powi(g, len - 1 - t) : 0.f;
+        }
+    }
     f32x4 C[4][4];
     float sq[4];
 #pragma unroll
@@ -277,8 +304,7 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
         arow[tg] = Ag + (long)(tok_ok[tg] ? t : tb) * H + 8 * q4;
     }
     // k-step operands: attention values of the four token groups and the pool
-    // tiles; two buffers in turn, so one k-step's loads fly while the other
-    // k-step's MFMAs run
+    // tiles
     constexpr int AW = kPrecise ? 2 : 1;  // 16-byte loads per token group
     struct Ops {
         u32x4 a[4][AW];
@@ -299,12 +325,34 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
             }
         }
     };
-    auto compute_ops = [&](const Ops &o) {
+    auto compute_ops = [&](const Ops &o, int ks) {
         bf16x8 bh[4], bl[4];
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
             split_a8<TIn>(o.a[tg], bh[tg], bl[tg], sq[tg]);
             if (!tok_ok[tg]) bh[tg] = bl[tg] = bf16x8{};
+        }
+        if (fuse_agg) {
+            // Σ_t (1-γ)γ^(len-1-t)·a[t][x] over the lane's 4 tokens, then over
+            // the 16 lanes of its row; lane c16 = 0 parks the 8 sums in LDS
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = 0.f;
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) {
+                    float v;
+                    if constexpr (kPrecise) v = __uint_as_float(o.a[tg][e >> 2][e & 3]);
+                    else v = (e & 1) ? bf16_hi(o.a[tg][0][e >> 1]) : bf16_lo(o.a[tg][0][e >> 1]);
+                    p[e] = fmaf(om[tg], v, p[e]);
+                }
+                p[e] = row_sum16(p[e]);
+            }
+            if (c16 == 0) {
+                float *d = aggS + 32 * ks + 8 * q4;
+                *reinterpret_cast<float4 *>(d) = make_float4(p[0], p[1], p[2], p[3]);
+                *reinterpret_cast<float4 *>(d + 4) = make_float4(p[4], p[5], p[6], p[7]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -318,21 +366,28 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
             }
         }
     };
-    {
+    {   // two buffers in turn: one k-step's loads fly while the other's MFMAs run
         Ops o0, o1;
         if (ks0 < ks1) load_ops(ks0, o0);
         for (int ks = ks0; ks < ks1; ks += 2) {
             if (ks + 1 < ks1) load_ops(ks + 1, o1);
-            compute_ops(o0);
+            compute_ops(o0, ks);
             if (ks + 1 >= ks1) break;
             if (ks + 2 < ks1) load_ops(ks + 2, o0);
-            compute_ops(o1);
+            compute_ops(o1, ks + 1);
         }
     }
-    // the reciprocal norms of this lane's 16 slots go out before the exchange
+    // the reciprocal norms of this lane's 16 slots
     float isn[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) isn[k] = sinv[16 * (k >> 2) + 4 * q4 + (k & 3)];
+    if (fuse_agg) {  // the tile's field aggregate, all H columns
+        __syncthreads();
+        float *dst = a.agg64 + ((long)l * a.ntiles + tile) * H;
+        for (int x = 4 * threadIdx.x; x < H; x += 4 * 256)
+            *reinterpret_cast<float4 *>(dst + x) = *reinterpret_cast<const float4 *>(aggS + x);
+        __syncthreads();  // the exchange below reuses the buffer
+    }
 
     // ---- (2) reduce the four partials: wave w ends with token group tg = w -------
     f32x4 Cw[4];
@@ -418,22 +473,25 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kCB = 128;       // columns per workgroup
 constexpr int kCoefEnt = 8;    // (token group, k-step) pairs of the band/field operand
-constexpr int kTabEntries = (kCoefEnt * 2 + 4) * 64;  // coefficient + identity operands (u32x4)
+constexpr int kTabEntries = kCoefEnt * 2 * 64;  // band/field operands (u32x4)
 // token group tg uses the k-steps s = 0 .. kSteps[tg]-1 (staged rows 32s .. 32s+31),
 // table entries {0, 1, 3, 5}[tg] + s; its own tokens sit in k-step kIdStep[tg]
 
 template <typename TIn>
 struct ColLayout;
+// kRows: staged tokens per staging item (one 16-byte piece of each), moved into
+// LDS as one 16-byte write per column
 template <>
 struct ColLayout<__bf16> {
-    // column c: chunk b (staged tokens 8b .. 8b+7, 16 bytes) at 16·(b ^ ((c >> 3) & 3))
-    static constexpr int kColBytes = 192;
-    __device__ static int chunk(int c, int b) { return c * kColBytes + 16 * (b ^ ((c >> 3) & 3)); }
+    // column c: chunk b (staged tokens 8b .. 8b+7, 16 bytes) at 16·(b ^ ((4c + c/8) mod 16));
+    // both the staging writes and the operand reads meet 16 distinct bank quads
+    static constexpr int kColBytes = 256, kRows = 8;
+    __device__ static int chunk(int c, int b) { return c * kColBytes + 16 * (b ^ ((4 * c + (c >> 3)) & 15)); }
 };
 template <>
 struct ColLayout<float> {
     // column c: chunk b (staged tokens 4b .. 4b+3, 16 bytes) at 16·b
-    static constexpr int kColBytes = 336;
+    static constexpr int kColBytes = 336, kRows = 4;
     __device__ static int chunk(int c, int b) { return c * kColBytes + 16 * b; }
 };
 
@@ -452,10 +510,10 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     constexpr int kRowsE = kBlk + kTile;     // staged tokens tb-16 .. tb+63
     constexpr int EPC = 16 / sizeof(TIn);    // columns per 16-byte piece
     constexpr int CPR = kCB / EPC;           // pieces per staged row
-    constexpr int NITEM = kRowsE / 4 * CPR;  // staging items: 4 tokens x one piece
+    constexpr int RPI = LY::kRows;             // staged tokens per item
+    constexpr int NITEM = kRowsE / RPI * CPR;  // staging items: RPI tokens x one piece
     constexpr int NIT = (NITEM + 255) / 256;
-    static_assert(NITEM % 64 == 0, "a partial item round must cover whole waves");
-    constexpr int NTAB = (kPrecise ? kCoefEnt * 2 : kCoefEnt * 2 + 4) * 64;
+    constexpr int NTAB = kTabEntries;
     static_assert(NTAB % 256 == 0, "table copy must split evenly");
     constexpr int kSteps[4] = {1, 2, 2, 3}, kIdStep[4] = {0, 1, 1, 2};
     constexpr int OW = 2 * (int)sizeof(TOut);  // output dwords per 8 values
@@ -478,16 +536,16 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     const TIn *Ag = reinterpret_cast<const TIn *>(a.attn) + (long)l * T * H;
 
     // ---- (1) loads: staging items, the operand table, pool^T, field carry ----
-    u32x4 stg[NIT][4];
+    u32x4 stg[NIT][RPI];
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
         const int it = threadIdx.x + 256 * k;
-        if (it < NITEM) {  // wave-uniform
+        if (it < NITEM) {
             const int rq = it / CPR, cp = it % CPR;
             const int col = xb + cp * EPC;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tb - kBlk + 4 * rq + i;
+            for (int i = 0; i < RPI; ++i) {
+                const int t = tb - kBlk + RPI * rq + i;
                 stg[k][i] = u32x4{0u, 0u, 0u, 0u};
                 if (t >= 0 && t < T && col < H) stg[k][i] = *reinterpret_cast<const u32x4 *>(Ag + (long)t * H + col);
             }
@@ -498,7 +556,8 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     for (int k = 0; k < NTAB / 256; ++k) tab[k] = reinterpret_cast<const u32x4 *>(a.coef)[threadIdx.x + 256 * k];
     const int pl = a.pool_stride == 0 ? 0 : l;
     const uint16_t *poolT = a.poolT + (long)pl * (H / 16) * 2 * 2 * kOpElems + lane * 8;
-    bf16x8 pt[2][2][2];  // [half][slot k-step][hi/lo]
+    constexpr int SL = 2;  // the semantic operands as bf16 hi + lo
+    bf16x8 pt[2][2][SL];  // [half][slot k-step][hi/lo]
     float Fc[8];
     if (has) {
 #pragma unroll
@@ -506,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
 #pragma unroll
             for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
+                for (int hl = 0; hl < SL; ++hl)
                     pt[h][sk][hl] = get8(poolT + (((long)(xw / 16 + h) * 2 + sk) * 2 + hl) * kOpElems);
         const float *carry = a.carry + (long)lt * H + x0;
 #pragma unroll
@@ -518,11 +577,13 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     // semantic weights of the tile, B operands [tg][ks][hi/lo]: two token groups
     // ahead, the next pair as each group finishes with its own
     const uint16_t *wsem = a.wsem + (long)lt * 4 * 4 * kOpElems + lane * 8;
-    bf16x8 wb[2][4];
+    bf16x8 wb[2][2][SL];  // [buffer][slot k-step][hi/lo]
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int o = 0; o < 4; ++o) wb[b][o] = get8(wsem + (b * 4 + o) * kOpElems);
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int hl = 0; hl < SL; ++hl) wb[b][ks][hl] = get8(wsem + (b * 4 + ks * 2 + hl) * kOpElems);
 
     // ---- (2) staging -> column-major LDS tile; table -> LDS ------------------
 #pragma unroll
@@ -531,19 +592,17 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
         if (it < NITEM) {
             const int rq = it / CPR, cp = it % CPR;
             if constexpr (!kPrecise) {
-                // 4 tokens x 8 columns: per column the 4 tokens as one 8-byte write
+                // 8 tokens x 8 columns, transposed: per column the 8 tokens as one chunk
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int wd = e >> 1;
-                    u32x2 v;
-                    if (e & 1) {
-                        v[0] = (stg[k][0][wd] >> 16) | (stg[k][1][wd] & 0xffff0000u);
-                        v[1] = (stg[k][2][wd] >> 16) | (stg[k][3][wd] & 0xffff0000u);
-                    } else {
-                        v[0] = (stg[k][0][wd] & 0xffffu) | (stg[k][1][wd] << 16);
-                        v[1] = (stg[k][2][wd] & 0xffffu) | (stg[k][3][wd] << 16);
-                    }
-                    *reinterpret_cast<u32x2 *>(AsT + LY::chunk(cp * 8 + e, rq >> 1) + 8 * (rq & 1)) = v;
+                    // bytes of the low (e even) or high (e odd) halves of two rows
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                    u32x4 v;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        v[d] = __builtin_amdgcn_perm(stg[k][2 * d + 1][wd], stg[k][2 * d][wd], sel);
+                    *reinterpret_cast<u32x4 *>(AsT + LY::chunk(cp * 8 + e, rq)) = v;
                 }
             } else {
                 // 4 tokens x 4 columns: per column one 16-byte write
@@ -589,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     // ---- (4) per token group: contraction, epilogue; outputs held until the end
     const float g = a.ema_gamma;
     const float invR = 1.f / (float)R;
-    const float al = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
+    const float al = load_uniform(a.alpha_tab + l);  // α of this layer
     const float gc = powi(g, c16 + 1), g16 = powi(g, kBlk);
     const float *ringl = a.ring + (long)l * R * H;
     const int ring0 = a.t0 % R;  // slot of relative token 0
@@ -599,10 +658,15 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     for (int tg = 0; tg < 4; ++tg) {
         if (16 * tg >= len) break;  // wave-uniform
         const int t = 16 * tg + c16;  // this lane's token (tile-relative)
-        const bf16x8 wh0 = wb[tg & 1][0], wl0 = wb[tg & 1][1], wh1 = wb[tg & 1][2], wl1 = wb[tg & 1][3];
+        // the accumulator starts from the field carried into the tile, 0.5·γ^(t+1)·F
+        const float cF = 0.5f * gc * powi(g16, tg);
         f32x4 D[2], Da[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) D[h] = Da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) D[h][i] = cF * Fc[4 * h + i];
+            Da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int st = 0; st < kSteps[tg]; ++st) {
             const int ent = (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5) + st;
@@ -618,28 +682,38 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
         // 0.5·semantic: pool^T · (0.5 w)^T, both split into bf16 hi + lo
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            D[h] = mfma_bf16_16x16x32(pt[h][0][0], wh0, D[h]);
-            D[h] = mfma_bf16_16x16x32(pt[h][0][0], wl0, D[h]);
-            D[h] = mfma_bf16_16x16x32(pt[h][0][1], wh0, D[h]);
-            D[h] = mfma_bf16_16x16x32(pt[h][1][0], wh1, D[h]);
-            D[h] = mfma_bf16_16x16x32(pt[h][1][0], wl1, D[h]);
-            D[h] = mfma_bf16_16x16x32(pt[h][1][1], wh1, D[h]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 *w = wb[tg & 1][ks];
+                D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[0], D[h]);
+                D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[1], D[h]);
+                D[h] = mfma_bf16_16x16x32(pt[h][ks][1], w[0], D[h]);
+            }
         }
         if (tg + 2 < 4) {  // every tile has all four groups' weights
 #pragma unroll
-            for (int o = 0; o < 4; ++o) wb[tg & 1][o] = get8(wsem + ((tg + 2) * 4 + o) * kOpElems);
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hl = 0; hl < SL; ++hl)
+                    wb[tg & 1][ks][hl] = get8(wsem + ((tg + 2) * 4 + ks * 2 + hl) * kOpElems);
         }
-        if constexpr (!kPrecise) {  // a itself through the identity operand
-            const bf16x8 id = __builtin_bit_cast(bf16x8, TabS[(kCoefEnt * 2 + tg) * 64 + lane]);
+        if constexpr (!kPrecise) {
+            // a itself through the identity operand: B[k][n] = 1 where staged row
+            // 32·kIdStep + k is token n of the group (row 16 + 16tg + n)
+            const int eid = kBlk + 16 * tg + c16 - 32 * kIdStep[tg] - 8 * q4;  // this lane's 1, if 0..7
+            const uint32_t one = eid & 1 ? 0x3f800000u : 0x3f80u;
+            u32x4 idw;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) idw[d] = (eid >= 0 && eid < 8 && (eid >> 1) == d) ? one : 0u;
+            const bf16x8 id = __builtin_bit_cast(bf16x8, idw);
 #pragma unroll
             for (int h = 0; h < 2; ++h) Da[h] = mfma_bf16_16x16x32(Av[kIdStep[tg]][h], id, Da[h]);
         }
         // epilogue for the lane's 8 columns of token t
-        const float cF = 0.5f * gc * powi(g16, tg);
-        float halo[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) halo[k] = 0.f;
         if (tg == 0 && tile == 0 && t < R - 1) {
+            float halo[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) halo[k] = 0.f;
             // the band's tokens before the call: the carried ring, slot (t0 + j) mod R
             for (int j = t - R + 1; j < 0; ++j) {
                 const int slot = ring0 + j < 0 ? ring0 + j + R : ring0 + j;
@@ -650,12 +724,14 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
                     halo[k] += r4.x; halo[k + 1] += r4.y; halo[k + 2] += r4.z; halo[k + 3] += r4.w;
                 }
             }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) D[k >> 2][k & 3] += halo[k] * invR;
         }
         float o[8], en[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int h = k >> 2, i = k & 3;
-            const float e = fminf(fmaxf(D[h][i] + cF * Fc[k] + halo[k] * invR, -a.clip), a.clip);
+            const float e = fminf(fmaxf(D[h][i], -a.clip), a.clip);
             en[k] = al * e;
             float av;
             if constexpr (kPrecise) {
@@ -664,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
             } else {
                 av = Da[h][i];
             }
-            o[k] = av + en[k];
+            o[k] = fmaf(al, e, av);
         }
         if constexpr (std::is_same<TOut, float>::value) {
 #pragma unroll
@@ -709,32 +785,26 @@ __global__ __launch_bounds__(256) void k_ring_out(EnhanceArgs a) {
 }
 
 // per-slot reciprocal norms: one workgroup per (pool layer, slot); the workgroups past
-// them write the band/field and identity operands of k_cols (the same for
-// every layer and tile): entry (e, hi/lo) for e = {0, 1, 3, 5}[tg] + s, then
-// the identities of the four token groups
+// them write the band/field operands of k_cols (the same for every layer and
+// tile), entry (e, hi/lo) for e = {0, 1, 3, 5}[tg] + s, and α of each layer
 __global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
     __shared__ float red[4];
     const int nsn = a.n_pool_layers * kSlots;
+    if ((int)blockIdx.x >= nsn + kTabEntries / 256) {  // α of each layer of the call
+        const int l = ((int)blockIdx.x - nsn - kTabEntries / 256) * 256 + threadIdx.x;
+        if (l < a.L) a.alpha_tab[l] = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
+        return;
+    }
     if ((int)blockIdx.x >= nsn) {
         const int idx = ((int)blockIdx.x - nsn) * 256 + threadIdx.x;
         const int ln = idx % 64;
+        const int ent = idx / 128, hl = (idx / 64) & 1;
+        const int tg = ent >= 5 ? 3 : ent >= 3 ? 2 : ent >= 1 ? 1 : 0;
+        const int st = ent - (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5);
         float v[8];
-        int hl = 0;
-        if (idx < kCoefEnt * 2 * 64) {
-            const int ent = idx / 128;
-            hl = (idx / 64) & 1;
-            const int tg = ent >= 5 ? 3 : ent >= 3 ? 2 : ent >= 1 ? 1 : 0;
-            const int st = ent - (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = band_field_coef(16 * tg + (ln & 15), 32 * st + 8 * (ln >> 4) + e, a.R, a.ema_gamma);
-        } else {
-            const int tg = (idx - kCoefEnt * 2 * 64) / 64;
-            const int st = tg == 0 ? 0 : tg == 3 ? 2 : 1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = (32 * st + 8 * (ln >> 4) + e == kBlk + 16 * tg + (ln & 15)) ? 1.f : 0.f;
-        }
+        for (int e = 0; e < 8; ++e)
+            v[e] = band_field_coef(16 * tg + (ln & 15), 32 * st + 8 * (ln >> 4) + e, a.R, a.ema_gamma);
         uint16_t hi[8], lo[8], pick[8];
         split8(v, hi, lo);
 #pragma unroll
@@ -758,12 +828,15 @@ __global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
 template <typename TIn, typename TOut>
 hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_pool_prep, dim3(a.n_pool_layers * (a.H / 32)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_slot_norm, dim3(a.n_pool_layers * kSlots + kTabEntries / 256), dim3(256), 0, stream, a);
-    const int fchunks = a.H / (16 / (int)sizeof(TIn));
-    hipLaunchKernelGGL((k_field_agg<TIn>), dim3(a.L * a.ntiles * ((fchunks + 255) / 256)), dim3(256), 0,
-                       stream, a);
-    hipLaunchKernelGGL(k_field_carry, dim3(a.L * ((a.H + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_slot_norm, dim3(a.n_pool_layers * kSlots + kTabEntries / 256 + (a.L + 255) / 256),
+                       dim3(256), 0, stream, a);
+    if (a.H > kAggMaxH) {  // k_sem computes the tile aggregates itself up to kAggMaxH
+        const int fchunks = a.H / (16 / (int)sizeof(TIn));
+        hipLaunchKernelGGL((k_field_agg<TIn>), dim3(a.L * a.ntiles * ((fchunks + 255) / 256)), dim3(256), 0,
+                           stream, a);
+    }
     hipLaunchKernelGGL((k_sem<TIn>), dim3(a.L * a.ntiles), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_field_carry, dim3(a.L * ((a.H + 255) / 256)), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((k_cols<TIn, TOut>), dim3(a.L * a.ntiles * ((a.H + kCB - 1) / kCB)), dim3(256), 0,
                        stream, a);
     hipLaunchKernelGGL((k_ring_out<TIn>), dim3(a.L * a.R), dim3(256), 0, stream, a);
@@ -780,7 +853,9 @@ size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers) {
     // semantic weights: per tile 4 token groups x 2 k-steps x hi/lo x 512 bf16;
     // the band/field and identity operand table
     const size_t wsem = (size_t)L * nt * 4 * 4 * kOpElems + (size_t)kTabEntries * 8;
-    return floats * sizeof(float) + (ops + wsem) * sizeof(uint16_t);
+    // α per layer, rounded up to 64 floats
+    const size_t alphas = ((size_t)L + 63) / 64 * 64;
+    return (floats + alphas) * sizeof(float) + (ops + wsem) * sizeof(uint16_t);
 }
 
 hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream) {

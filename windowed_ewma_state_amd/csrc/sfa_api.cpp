@@ -235,6 +235,7 @@ int sfa_enhance(const void *attn, void *out, float *ring, float *field, const fl
     a.poolT = a.poolA + (size_t)n_pool_layers * H * 128;
     a.wsem = a.poolT + (size_t)n_pool_layers * H * 128;
     a.coef = a.wsem + (size_t)L * a.ntiles * 4 * 4 * 512;
+    a.alpha_tab = reinterpret_cast<float *>(a.coef + (size_t)8 * 2 * 64 * 8);
     return hip_status(sfa::launch_enhance(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -78,7 +78,8 @@ struct EnhanceArgs {
     uint16_t *poolA;        // [n_pool_layers][H/32][4][2][64][8] bf16 hi/lo, cosine operand
     uint16_t *poolT;        // [n_pool_layers][H/16][2][2][64][8] bf16 hi/lo, semantic operand
     uint16_t *wsem;         // [L][ntiles][4][2][2][64][8] bf16 hi/lo of 0.5·(slot weights)
-    uint16_t *coef;         // [(8 x 2) + 4][64][8] band/field and identity operands
+    uint16_t *coef;         // [8 x 2][64][8] band/field operands
+    float *alpha_tab;       // [L] α of each layer of the call
 };
 size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers);
 hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream);

@@ -469,7 +469,8 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
 //         [+ the carried ring's share of the band in the call's first tile],
 //   out = a + α_l·clip(e).
 // Every load is issued before the first output store (outputs wait in
-// registers until the end), so no wait for a load ever waits for a store.
+// registers until the end), so no wait for a load ever waits for a store;
+// the outputs leave through LDS as whole rows (full 128-byte lines).
 // ---------------------------------------------------------------------------
 constexpr int kCB = 128;       // columns per workgroup
 constexpr int kCoefEnt = 8;    // (token group, k-step) pairs of the band/field operand
@@ -517,7 +518,10 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     static_assert(NTAB % 256 == 0, "table copy must split evenly");
     constexpr int kSteps[4] = {1, 2, 2, 3}, kIdStep[4] = {0, 1, 1, 2};
     constexpr int OW = 2 * (int)sizeof(TOut);  // output dwords per 8 values
-    __shared__ __attribute__((aligned(16))) unsigned char AsT[kCB * LY::kColBytes];
+    // the staged tile, and at the end the output tile (row-major, 16-byte padded rows)
+    constexpr int kAsBytes = kCB * LY::kColBytes > kTile * (kCB * (int)sizeof(TOut) + 16)
+                                 ? kCB * LY::kColBytes : kTile * (kCB * (int)sizeof(TOut) + 16);
+    __shared__ __attribute__((aligned(16))) unsigned char AsT[kAsBytes];
     __shared__ __attribute__((aligned(16))) u32x4 TabS[NTAB];
 
     const int ncb = (a.H + kCB - 1) / kCB;
@@ -616,159 +620,169 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
 #pragma unroll
     for (int k = 0; k < NTAB / 256; ++k) TabS[threadIdx.x + 256 * k] = tab[k];
     __syncthreads();
-    if (!has) return;  // no barrier follows
-
-    // ---- (3) A operands: the staged values, row m of half h = column 8(m/4) + 4h + m%4
-    bf16x8 Av[3][2], Al[kPrecise ? 3 : 1][2];
+    uint32_t ob[4][OW];  // outputs of the lane's 8 columns per token group
+    if (has) {  // wave-uniform: a partial last block leaves waves without columns
+        // ---- (3) A operands: the staged values, row m of half h = column 8(m/4) + 4h + m%4
+        bf16x8 Av[3][2], Al[kPrecise ? 3 : 1][2];
 #pragma unroll
-    for (int st = 0; st < 3; ++st)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = 32 * wave + 8 * (c16 >> 2) + 4 * h + (c16 & 3);
-            int b = 4 * st + q4;  // 8-token chunk; past the 80 staged tokens read 16 earlier
-            if (b >= kRowsE / 8) b -= 2;  // (their coefficients are zero)
-            if constexpr (!kPrecise) {
-                Av[st][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, b)));
-            } else {
-                const u32x4 w0 = *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, 2 * b));
-                const u32x4 w1 = *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, 2 * b + 1));
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = __uint_as_float(w0[e]);
-                    v[4 + e] = __uint_as_float(w1[e]);
-                }
-                uint16_t hi[8], lo[8];
-                split8(v, hi, lo);
-                Av[st][h] = get8(hi);
-                Al[st][h] = get8(lo);
-            }
-        }
-
-    // ---- (4) per token group: contraction, epilogue; outputs held until the end
-    const float g = a.ema_gamma;
-    const float invR = 1.f / (float)R;
-    const float al = load_uniform(a.alpha_tab + l);  // α of this layer
-    const float gc = powi(g, c16 + 1), g16 = powi(g, kBlk);
-    const float *ringl = a.ring + (long)l * R * H;
-    const int ring0 = a.t0 % R;  // slot of relative token 0
-    float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
-    uint32_t ob[4][OW];
-#pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-        if (16 * tg >= len) break;  // wave-uniform
-        const int t = 16 * tg + c16;  // this lane's token (tile-relative)
-        // the accumulator starts from the field carried into the tile, 0.5·γ^(t+1)·F
-        const float cF = 0.5f * gc * powi(g16, tg);
-        f32x4 D[2], Da[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) D[h][i] = cF * Fc[4 * h + i];
-            Da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int st = 0; st < kSteps[tg]; ++st) {
-            const int ent = (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5) + st;
-            const bf16x8 ch_ = __builtin_bit_cast(bf16x8, TabS[(ent * 2) * 64 + lane]);
-            const bf16x8 cl_ = __builtin_bit_cast(bf16x8, TabS[(ent * 2 + 1) * 64 + lane]);
+        for (int st = 0; st < 3; ++st)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                D[h] = mfma_bf16_16x16x32(Av[st][h], ch_, D[h]);
-                D[h] = mfma_bf16_16x16x32(Av[st][h], cl_, D[h]);
-                if constexpr (kPrecise) D[h] = mfma_bf16_16x16x32(Al[st][h], ch_, D[h]);
-            }
-        }
-        // 0.5·semantic: pool^T · (0.5 w)^T, both split into bf16 hi + lo
+                const int c = 32 * wave + 8 * (c16 >> 2) + 4 * h + (c16 & 3);
+                int b = 4 * st + q4;  // 8-token chunk; past the 80 staged tokens read 16 earlier
+                if (b >= kRowsE / 8) b -= 2;  // (their coefficients are zero)
+                if constexpr (!kPrecise) {
+                    Av[st][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, b)));
+                } else {
+                    const u32x4 w0 = *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, 2 * b));
+                    const u32x4 w1 = *reinterpret_cast<const u32x4 *>(AsT + LY::chunk(c, 2 * b + 1));
+                    float v[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 *w = wb[tg & 1][ks];
-                D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[0], D[h]);
-                D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[1], D[h]);
-                D[h] = mfma_bf16_16x16x32(pt[h][ks][1], w[0], D[h]);
-            }
-        }
-        if (tg + 2 < 4) {  // every tile has all four groups' weights
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int hl = 0; hl < SL; ++hl)
-                    wb[tg & 1][ks][hl] = get8(wsem + ((tg + 2) * 4 + ks * 2 + hl) * kOpElems);
-        }
-        if constexpr (!kPrecise) {
-            // a itself through the identity operand: B[k][n] = 1 where staged row
-            // 32·kIdStep + k is token n of the group (row 16 + 16tg + n)
-            const int eid = kBlk + 16 * tg + c16 - 32 * kIdStep[tg] - 8 * q4;  // this lane's 1, if 0..7
-            const uint32_t one = eid & 1 ? 0x3f800000u : 0x3f80u;
-            u32x4 idw;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) idw[d] = (eid >= 0 && eid < 8 && (eid >> 1) == d) ? one : 0u;
-            const bf16x8 id = __builtin_bit_cast(bf16x8, idw);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) Da[h] = mfma_bf16_16x16x32(Av[kIdStep[tg]][h], id, Da[h]);
-        }
-        // epilogue for the lane's 8 columns of token t
-        if (tg == 0 && tile == 0 && t < R - 1) {
-            float halo[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) halo[k] = 0.f;
-            // the band's tokens before the call: the carried ring, slot (t0 + j) mod R
-            for (int j = t - R + 1; j < 0; ++j) {
-                const int slot = ring0 + j < 0 ? ring0 + j + R : ring0 + j;
-                const float *rr = ringl + (long)slot * H + x0;
-#pragma unroll
-                for (int k = 0; k < 8; k += 4) {
-                    const float4 r4 = *reinterpret_cast<const float4 *>(rr + k);
-                    halo[k] += r4.x; halo[k + 1] += r4.y; halo[k + 2] += r4.z; halo[k + 3] += r4.w;
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = __uint_as_float(w0[e]);
+                        v[4 + e] = __uint_as_float(w1[e]);
+                    }
+                    uint16_t hi[8], lo[8];
+                    split8(v, hi, lo);
+                    Av[st][h] = get8(hi);
+                    Al[st][h] = get8(lo);
                 }
             }
+
+        // ---- (4) per token group: contraction, epilogue; outputs held until the end
+        const float g = a.ema_gamma;
+        const float invR = 1.f / (float)R;
+        const float al = load_uniform(a.alpha_tab + l);  // α of this layer
+        const float gc = powi(g, c16 + 1), g16 = powi(g, kBlk);
+        const float *ringl = a.ring + (long)l * R * H;
+        const int ring0 = a.t0 % R;  // slot of relative token 0
+        float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) D[k >> 2][k & 3] += halo[k] * invR;
-        }
-        float o[8], en[8];
+        for (int tg = 0; tg < 4; ++tg) {
+            if (16 * tg >= len) break;  // wave-uniform
+            const int t = 16 * tg + c16;  // this lane's token (tile-relative)
+            // the accumulator starts from the field carried into the tile, 0.5·γ^(t+1)·F
+            const float cF = 0.5f * gc * powi(g16, tg);
+            f32x4 D[2], Da[2];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int h = k >> 2, i = k & 3;
-            const float e = fminf(fmaxf(D[h][i], -a.clip), a.clip);
-            en[k] = al * e;
-            float av;
-            if constexpr (kPrecise) {
-                const int c = 32 * wave + 8 * q4 + k, r = kBlk + t;
-                av = *reinterpret_cast<const float *>(AsT + LY::chunk(c, r >> 2) + 4 * (r & 3));
-            } else {
-                av = Da[h][i];
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) D[h][i] = cF * Fc[4 * h + i];
+                Da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            o[k] = fmaf(al, e, av);
-        }
-        if constexpr (std::is_same<TOut, float>::value) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) ob[tg][k] = __float_as_uint(o[k]);
-        } else {
+            for (int st = 0; st < kSteps[tg]; ++st) {
+                const int ent = (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5) + st;
+                const bf16x8 ch_ = __builtin_bit_cast(bf16x8, TabS[(ent * 2) * 64 + lane]);
+                const bf16x8 cl_ = __builtin_bit_cast(bf16x8, TabS[(ent * 2 + 1) * 64 + lane]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ob[tg][i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
-        }
-        if (Eg && tb + t < T) {
-            float *ed = Eg + (long)(tb + t) * H + x0;
-            *reinterpret_cast<float4 *>(ed) = make_float4(en[0], en[1], en[2], en[3]);
-            *reinterpret_cast<float4 *>(ed + 4) = make_float4(en[4], en[5], en[6], en[7]);
+                for (int h = 0; h < 2; ++h) {
+                    D[h] = mfma_bf16_16x16x32(Av[st][h], ch_, D[h]);
+                    D[h] = mfma_bf16_16x16x32(Av[st][h], cl_, D[h]);
+                    if constexpr (kPrecise) D[h] = mfma_bf16_16x16x32(Al[st][h], ch_, D[h]);
+                }
+            }
+            // 0.5·semantic: pool^T · (0.5 w)^T, both split into bf16 hi + lo
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 *w = wb[tg & 1][ks];
+                    D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[0], D[h]);
+                    D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[1], D[h]);
+                    D[h] = mfma_bf16_16x16x32(pt[h][ks][1], w[0], D[h]);
+                }
+            }
+            if (tg + 2 < 4) {  // every tile has all four groups' weights
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int hl = 0; hl < SL; ++hl)
+                        wb[tg & 1][ks][hl] = get8(wsem + ((tg + 2) * 4 + ks * 2 + hl) * kOpElems);
+            }
+            if constexpr (!kPrecise) {
+                // a itself through the identity operand: B[k][n] = 1 where staged row
+                // 32·kIdStep + k is token n of the group (row 16 + 16tg + n)
+                const int eid = kBlk + 16 * tg + c16 - 32 * kIdStep[tg] - 8 * q4;  // this lane's 1, if 0..7
+                const uint32_t one = eid & 1 ? 0x3f800000u : 0x3f80u;
+                u32x4 idw;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) idw[d] = (eid >= 0 && eid < 8 && (eid >> 1) == d) ? one : 0u;
+                const bf16x8 id = __builtin_bit_cast(bf16x8, idw);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) Da[h] = mfma_bf16_16x16x32(Av[kIdStep[tg]][h], id, Da[h]);
+            }
+            // epilogue for the lane's 8 columns of token t
+            if (tg == 0 && tile == 0 && t < R - 1) {
+                float halo[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) halo[k] = 0.f;
+                // the band's tokens before the call: the carried ring, slot (t0 + j) mod R
+                for (int j = t - R + 1; j < 0; ++j) {
+                    const int slot = ring0 + j < 0 ? ring0 + j + R : ring0 + j;
+                    const float *rr = ringl + (long)slot * H + x0;
+#pragma unroll
+                    for (int k = 0; k < 8; k += 4) {
+                        const float4 r4 = *reinterpret_cast<const float4 *>(rr + k);
+                        halo[k] += r4.x; halo[k + 1] += r4.y; halo[k + 2] += r4.z; halo[k + 3] += r4.w;
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) D[k >> 2][k & 3] += halo[k] * invR;
+            }
+            float o[8], en[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int h = k >> 2, i = k & 3;
+                const float e = fminf(fmaxf(D[h][i], -a.clip), a.clip);
+                en[k] = al * e;
+                float av;
+                if constexpr (kPrecise) {
+                    const int c = 32 * wave + 8 * q4 + k, r = kBlk + t;
+                    av = *reinterpret_cast<const float *>(AsT + LY::chunk(c, r >> 2) + 4 * (r & 3));
+                } else {
+                    av = Da[h][i];
+                }
+                o[k] = fmaf(al, e, av);
+            }
+            if constexpr (std::is_same<TOut, float>::value) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) ob[tg][k] = __float_as_uint(o[k]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ob[tg][i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
+            }
+            if (Eg && tb + t < T) {
+                float *ed = Eg + (long)(tb + t) * H + x0;
+                *reinterpret_cast<float4 *>(ed) = make_float4(en[0], en[1], en[2], en[3]);
+                *reinterpret_cast<float4 *>(ed + 4) = make_float4(en[4], en[5], en[6], en[7]);
+            }
         }
     }
-    // ---- (5) output rows: 8 consecutive columns per lane -----------------------
+    // ---- (5) the output tile through LDS, then whole rows per 16 lanes -----------
+    constexpr int ORB = kCB * (int)sizeof(TOut) + 16;  // LDS row stride of the output tile (bytes)
+    constexpr int PPR = kCB * (int)sizeof(TOut) / 16;  // 16-byte pieces per output row
     TOut *Og = reinterpret_cast<TOut *>(a.out) + (long)l * T * H;
+    __syncthreads();  // every wave is done with the staged tile
+    if (has) {
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-        if (16 * tg >= len) break;
-        const int t = tb + 16 * tg + c16;
-        if (t < T) {
-            TOut *dst = Og + (long)t * H + x0;
+        for (int tg = 0; tg < 4; ++tg) {
+            if (16 * tg >= len) break;
+            unsigned char *d = AsT + (16 * tg + c16) * ORB + (32 * wave + 8 * q4) * (int)sizeof(TOut);
 #pragma unroll
             for (int k = 0; k < OW / 4; ++k)
-                st_stream(reinterpret_cast<unsigned char *>(dst) + 16 * k,
-                          u32x4{ob[tg][4 * k], ob[tg][4 * k + 1], ob[tg][4 * k + 2], ob[tg][4 * k + 3]});
+                *reinterpret_cast<u32x4 *>(d + 16 * k) =
+                    u32x4{ob[tg][4 * k], ob[tg][4 * k + 1], ob[tg][4 * k + 2], ob[tg][4 * k + 3]};
         }
     }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < len * PPR; idx += 256) {
+        const int r = idx / PPR, pc = idx % PPR;
+        const int col = xb + pc * (16 / (int)sizeof(TOut));
+        if (col < H)
+            st_stream(Og + (long)(tb + r) * H + col, *reinterpret_cast<const u32x4 *>(AsT + r * ORB + 16 * pc));
+    }
+
 }
 
 // last min(R, T) attention rows -> ring slots (t0 + t) mod R; one workgroup

@@ -363,6 +363,14 @@ __device__ __forceinline__ void late_load(const DecodeArgs &a, int unit, LateLoa
 // untouched): the store is issued all the same, 16 bytes per lane.
 __device__ __attribute__((aligned(256))) uint32_t g_decode_sink[kWave * 4];
 
+// each lane takes the four dwords of the lane 8 away within its 16-lane row
+__device__ __forceinline__ u32x4 row_ror8(u32x4 v) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0x128, 0xf, 0xf, true);
+    return r;
+}
+
 template <typename T>
 __device__ __forceinline__ T *sink_or(T *p, bool skip, int lane) {
     return skip ? reinterpret_cast<T *>(g_decode_sink + 4 * lane) : p;
@@ -522,6 +530,14 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
 
         const float al = u.al;
         TOut *orow = reinterpret_cast<TOut *>(a.out) + ((long)lb * a.Hq + G * group + hc) * D;
+        // up to 8 heads: lanes c16 >= 8 (duplicates otherwise) take over the next
+        // k-step (bf16) or the upper half (fp32) of head c16 - 8, rotated over by
+        // 8 lanes, so every store covers whole 128-byte lines of the output rows
+        constexpr bool kPairStore = QN * UnitLoads<D, QN>::RPI <= 8;
+        const bool upper = c16 >= 8;
+        TOut *orow2 = reinterpret_cast<TOut *>(a.out) +
+                      ((long)lb * a.Hq + G * group + min(c16 & 7, group - 1)) * D;
+        [[maybe_unused]] u32x4 wprev;  // bf16: the packed outputs of the even k-step
 #pragma unroll
         for (int k = 0; k < D / 32; ++k) {
             float ov[8];
@@ -548,7 +564,28 @@ __device__ __forceinline__ void unit_compute(const DecodeArgs &a, int unit, cons
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ov[4 * half + i] = fmaf(al, s4[i], o[i]);
             }
-            if constexpr (std::is_same<TOut, float>::value) {
+            if constexpr (kPairStore && std::is_same<TOut, float>::value) {
+                u32x4 lo4, hi4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo4[i] = __float_as_uint(ov[i]);
+                    hi4[i] = __float_as_uint(ov[4 + i]);
+                }
+                const u32x4 r = row_ror8(hi4);
+                *sink_or(reinterpret_cast<u32x4 *>(orow2 + 32 * k + 8 * q4 + (upper ? 4 : 0)), skip, lane) =
+                    upper ? r : lo4;
+            } else if constexpr (kPairStore) {
+                u32x4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
+                if (k & 1) {
+                    const u32x4 r = row_ror8(w);
+                    st_stream(sink_or(reinterpret_cast<u32x4 *>(orow2 + 32 * (upper ? k : k - 1) + 8 * q4), skip, lane),
+                              upper ? r : wprev);
+                } else {
+                    wprev = w;
+                }
+            } else if constexpr (std::is_same<TOut, float>::value) {
                 *sink_or(reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4), skip, lane) = make_float4(ov[0], ov[1], ov[2], ov[3]);
                 *sink_or(reinterpret_cast<float4 *>(orow + 32 * k + 8 * q4 + 4), skip, lane) = make_float4(ov[4], ov[5], ov[6], ov[7]);
             } else {

@@ -70,6 +70,10 @@ SMALL = [  # (L, T, H, n_slots, R, dtype)
     (2, 64, 64, 64, 1, torch.bfloat16), (3, 100, 128, 1, 4, torch.bfloat16),
     (1, 300, 1024, 64, 16, torch.bfloat16), (2, 257, 896, 33, 16, torch.bfloat16),
     (2, 70, 128, 64, 16, torch.float32), (1, 130, 64, 5, 3, torch.float32),
+    # the largest hidden size whose tile aggregates the slot-weight pass forms
+    # itself, and one above it (the separate aggregate pass)
+    (1, 70, 8192, 64, 16, torch.bfloat16), (1, 33, 8256, 64, 16, torch.bfloat16),
+    (1, 20, 8256, 64, 5, torch.float32),
 ]
 
 

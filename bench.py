@@ -367,7 +367,7 @@ def run_enhance(steps=20, warmup=3, sets=3):
     byts = enhance_bytes()
     return {"workload": "triple-channel enhancement, 24 layers x 4096 tokens, hidden 1024, 64 slots, bf16",
             "value": L * T / (ms * 1e-3), "unit": "tokens·layers/s", "us_per_call": ms * 1e3,
-            "kernel": "sfa_enhance (6 launches: pool operands, slot norms, k_sem, field carry, k_cols, ring)",
+            "kernel": "sfa_enhance (5 launches: pool operands and slot norms, k_sem, field carry, k_cols, ring)",
             "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
                          "unit": "GB/s", "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_call": byts}}
 

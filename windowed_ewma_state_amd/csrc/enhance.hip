@@ -12,9 +12,8 @@
 // slots, clip 0.5) are the SFA_Config of page "Signal Field Attention (SFA)".
 //
 // Launches:
-//   k_pool_prep    pool -> bf16 hi/lo in the two MFMA operand orders.
-//   k_slot_norm    1/|s| of every pool slot; the band/field operands;
-//                  α of each layer.
+//   k_prep         pool -> bf16 hi/lo in the two MFMA operand orders; 1/|s| of
+//                  every pool slot; the band/field operands; α of each layer.
 //   k_field_agg    EMA of each 64-token tile from zero (a thread per 16-byte
 //                  column chunk); only for hidden sizes above kAggMaxH.
 //   k_sem          one workgroup per (layer, 64-token tile): cosine scores
@@ -78,7 +77,7 @@ __device__ __forceinline__ bf16x8 get8(const uint16_t *src) {
 }
 
 // ---------------------------------------------------------------------------
-// k_pool_prep.  Per pool layer pl:
+// Pool operands (the first workgroups of k_prep).  Per pool layer pl:
 //   poolA[pl][ks][j][hl][lane][8]: slot 16j + lane%16, x = 32ks + 8(lane/16) + e
 //       (A operand of the cosine scores, k = hidden dim)
 //   poolT[pl][xg][ks][hl][lane][8]: x = 16xg + lane%16,
@@ -86,9 +85,9 @@ __device__ __forceinline__ bf16x8 get8(const uint16_t *src) {
 //       (A operand of the semantic sum, k = slot)
 // One workgroup per (pool layer, 32-column step); 256 threads = 4 j x 64 lanes.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_pool_prep(EnhanceArgs a) {
+__device__ __forceinline__ void pool_prep_block(const EnhanceArgs &a, int bid) {
     const int ksteps = a.H / 32;
-    const int pl = blockIdx.x / ksteps, ks = blockIdx.x % ksteps;
+    const int pl = bid / ksteps, ks = bid % ksteps;
     const float *P = a.pool + (long)pl * a.pool_stride;
     const int j = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int q4 = lane / 16, c16 = lane % 16;
@@ -182,34 +181,50 @@ __global__ __launch_bounds__(256) void k_field_agg(EnhanceArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_field_carry: field before each tile and the final field (thread per column)
+// k_field_carry: field before each tile and the final field.  One workgroup per
+// (layer, 32 columns); the tiles are split into 8 consecutive parts, each
+// folded on its own as (X, Γ) = (field from zero, product of decays), then
+// every part takes its carry-in from the parts before it (through LDS) and
+// writes the field before each of its tiles.
 // ---------------------------------------------------------------------------
+constexpr int kFcParts = 8, kFcCols = 32;
 __global__ __launch_bounds__(256) void k_field_carry(EnhanceArgs a) {
-    const int cpb = (a.H + 255) / 256;
+    __shared__ float pX[kFcParts][kFcCols], pG[kFcParts];
+    const int cpb = a.H / kFcCols;
     const int l = blockIdx.x / cpb;
-    const int x = (blockIdx.x % cpb) * 256 + threadIdx.x;
-    if (x >= a.H) return;
+    const int col = threadIdx.x % kFcCols, part = threadIdx.x / kFcCols;
+    const int x = (blockIdx.x % cpb) * kFcCols + col;
     const float g = a.ema_gamma;
     const float gfull = powi(g, kTile);
-    float F = a.field[(long)l * a.H + x];
-    const float *A = a.agg64 + (long)l * a.ntiles * a.H + x;
-    float *C = a.carry + (long)l * a.ntiles * a.H + x;
-    for (int i0 = 0; i0 < a.ntiles; i0 += kBlk) {
-        float ag[kBlk];
-#pragma unroll
-        for (int j = 0; j < kBlk; ++j) ag[j] = (i0 + j < a.ntiles) ? A[(long)(i0 + j) * a.H] : 0.f;
-#pragma unroll
-        for (int j = 0; j < kBlk; ++j) {
-            const int i = i0 + j;
-            if (i < a.ntiles) {
-                C[(long)i * a.H] = F;
-                const int len = min(kTile, a.T - i * kTile);
-                const float gl = len == kTile ? gfull : powi(g, len);
-                F = gl * F + ag[j];
-            }
-        }
+    const int nt = a.ntiles;
+    const int per = (nt + kFcParts - 1) / kFcParts;
+    const int i0 = min(part * per, nt), i1 = min(i0 + per, nt);
+    const float *A = a.agg64 + (long)l * nt * a.H + x;
+    float *C = a.carry + (long)l * nt * a.H + x;
+    auto decay = [&](int i) {
+        const int len = min(kTile, a.T - i * kTile);
+        return len == kTile ? gfull : powi(g, len);
+    };
+    float X = 0.f, Gm = 1.f;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+        const float gl = decay(i);
+        X = gl * X + A[(long)i * a.H];
+        Gm *= gl;
     }
-    a.field[(long)l * a.H + x] = F;
+    // the field before the call's first token, read by every part before the
+    // barrier that precedes the last part's write of the final field
+    float F = a.field[(long)l * a.H + x];
+    pX[part][col] = X;
+    if (col == 0) pG[part] = Gm;
+    __syncthreads();
+    for (int p = 0; p < part; ++p) F = pG[p] * F + pX[p][col];
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+        C[(long)i * a.H] = F;
+        F = decay(i) * F + A[(long)i * a.H];
+    }
+    if (i1 == nt && i0 < i1) a.field[(long)l * a.H + x] = F;  // the part holding the last tile
 }
 
 // ---------------------------------------------------------------------------
@@ -801,16 +816,16 @@ __global__ __launch_bounds__(256) void k_ring_out(EnhanceArgs a) {
 // per-slot reciprocal norms: one workgroup per (pool layer, slot); the workgroups past
 // them write the band/field operands of k_cols (the same for every layer and
 // tile), entry (e, hi/lo) for e = {0, 1, 3, 5}[tg] + s, and α of each layer
-__global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
+__device__ __forceinline__ void slot_norm_block(const EnhanceArgs &a, int bid) {
     __shared__ float red[4];
     const int nsn = a.n_pool_layers * kSlots;
-    if ((int)blockIdx.x >= nsn + kTabEntries / 256) {  // α of each layer of the call
-        const int l = ((int)blockIdx.x - nsn - kTabEntries / 256) * 256 + threadIdx.x;
+    if (bid >= nsn + kTabEntries / 256) {  // α of each layer of the call
+        const int l = (bid - nsn - kTabEntries / 256) * 256 + threadIdx.x;
         if (l < a.L) a.alpha_tab[l] = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
         return;
     }
-    if ((int)blockIdx.x >= nsn) {
-        const int idx = ((int)blockIdx.x - nsn) * 256 + threadIdx.x;
+    if (bid >= nsn) {
+        const int idx = (bid - nsn) * 256 + threadIdx.x;
         const int ln = idx % 64;
         const int ent = idx / 128, hl = (idx / 64) & 1;
         const int tg = ent >= 5 ? 3 : ent >= 3 ? 2 : ent >= 1 ? 1 : 0;
@@ -826,7 +841,7 @@ __global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
         put8(a.coef + (long)idx * 8, pick);
         return;
     }
-    const int pl = blockIdx.x / kSlots, slot = blockIdx.x % kSlots;
+    const int pl = bid / kSlots, slot = bid % kSlots;
     float ss = 0.f;
     if (slot < a.n_slots) {
         const float *P = a.pool + (long)pl * a.pool_stride + (long)slot * a.H;
@@ -839,10 +854,19 @@ __global__ __launch_bounds__(256) void k_slot_norm(EnhanceArgs a) {
         a.slot_norm[pl * kSlots + slot] = 1.f / fmaxf(sqrtf(red[0] + red[1] + red[2] + red[3]), 1e-12f);
 }
 
+// k_prep: the pool operands (the first n_pool_layers·H/32 workgroups) and the
+// slot norms, operand table and α (the rest), in one launch
+__global__ __launch_bounds__(256) void k_prep(EnhanceArgs a) {
+    const int npp = a.n_pool_layers * (a.H / 32);
+    if ((int)blockIdx.x < npp) pool_prep_block(a, blockIdx.x);
+    else slot_norm_block(a, blockIdx.x - npp);
+}
+
 template <typename TIn, typename TOut>
 hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(k_pool_prep, dim3(a.n_pool_layers * (a.H / 32)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_slot_norm, dim3(a.n_pool_layers * kSlots + kTabEntries / 256 + (a.L + 255) / 256),
+    hipLaunchKernelGGL(k_prep,
+                       dim3(a.n_pool_layers * (a.H / 32) + a.n_pool_layers * kSlots + kTabEntries / 256 +
+                            (a.L + 255) / 256),
                        dim3(256), 0, stream, a);
     if (a.H > kAggMaxH) {  // k_sem computes the tile aggregates itself up to kAggMaxH
         const int fchunks = a.H / (16 / (int)sizeof(TIn));
@@ -850,7 +874,7 @@ hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
                            stream, a);
     }
     hipLaunchKernelGGL((k_sem<TIn>), dim3(a.L * a.ntiles), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_field_carry, dim3(a.L * ((a.H + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_field_carry, dim3(a.L * (a.H / kFcCols)), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((k_cols<TIn, TOut>), dim3(a.L * a.ntiles * ((a.H + kCB - 1) / kCB)), dim3(256), 0,
                        stream, a);
     hipLaunchKernelGGL((k_ring_out<TIn>), dim3(a.L * a.R), dim3(256), 0, stream, a);

@@ -63,7 +63,7 @@ __device__ __forceinline__ void load_epl(const T *p, float *x) {
 // evicting steps of (1-γ)·γ^(later evicting steps)/m; m = p-W+1 at position p.
 // The kernel writes s and c per block and tile and β per tile.
 // ---------------------------------------------------------------------------
-template <typename TIn, int D, bool RM>
+template <typename TIn, int D, bool RM, bool QH>
 __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     constexpr int EPC = 16 / sizeof(TIn);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;           // chunks per row (8 or 16 for bf16, 16 or 32 for fp32)
@@ -72,16 +72,17 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tiles_per_bg = a.ntiles;
     // chain fastest: the waves of a workgroup take the same tile of consecutive
-    // (b, KV head) chains, i.e. neighbouring 256-byte pieces of the same rows
-    const int nbg = a.B * a.Hs;  // scan chains (b, S head)
+    // (b, KV head) pairs, i.e. neighbouring 256-byte pieces of the same rows.
+    // With γ per query head the wave folds its keys, loaded once, into the
+    // scan chain of every query head of the group.
+    const int nkv = a.B * a.Hkv;
     const int gt = blockIdx.x * 4 + wave;
-    if (gt >= nbg * tiles_per_bg) return;
-    const int tile = gt / nbg, bg = gt - tile * nbg;
-    const int b = bg / a.Hs, hs = bg % a.Hs;
-    const int G = a.s_per_query ? hs / a.group : hs;  // the KV head whose keys the chain folds
+    if (gt >= nkv * tiles_per_bg) return;
+    const int tile = gt / nkv, kvp = gt - tile * nkv;
+    const int b = kvp / a.Hkv, G = kvp % a.Hkv;
+    const int nh = QH ? a.group : 1;  // scan chains these keys feed
     const int n = a.n, W = a.W;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
-    const float gm = a.gamma[hs];
     const long row_stride = (long)a.Hkv * D;
     const TIn *Kbg = reinterpret_cast<const TIn *>(a.k) + ((long)b * n * a.Hkv + G) * D;
     const TIn *ringK = a.pos0 ? reinterpret_cast<const TIn *>(a.ring_k) + ((long)b * a.Hkv + G) * W * D : nullptr;
@@ -89,6 +90,27 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     const int tb = tile * kTile + kBlk * blk;
     const bool lane_ok = c0 < CPR;  // d = 64 bf16 has 8 chunks per row: half the lanes idle
 
+    // the keys this lane's block of 16 tokens evicts, loaded once
+    u32x4 raw[kBlk][CPL];
+    bool use[kBlk];
+#pragma unroll
+    for (int j = 0; j < kBlk; ++j) {
+        const int t = tb + j;
+        use[j] = lane_ok && (t < n) && (p0 + t >= W);
+        const TIn *row = use[j] ? kv_row(Kbg, row_stride, ringK, t - W, n, p0, W, D) : nullptr;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            raw[j][cc] = u32x4{0u, 0u, 0u, 0u};
+            if (row) raw[j][cc] = *reinterpret_cast<const u32x4 *>(row + (c0 + LPB * cc) * EPC);
+        }
+    }
+    __shared__ float blkv[4][4][D];  // [wave][block][d]
+    __shared__ float blkc[RM ? 4 : 1][4][RM ? D : 1];
+    __shared__ float decay[4][4], beta[4][4];
+    for (int jh = 0; jh < nh; ++jh) {
+    const int hs = QH ? G * a.group + jh : G;  // the scan chain's S head
+    const int bg = b * a.Hs + hs;
+    const float gm = a.gamma[hs];
     float A[CPL][EPC], Cs[RM ? CPL : 1][EPC];
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc)
@@ -101,19 +123,6 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
             for (int e = 0; e < EPC; ++e) Cs[cc][e] = 0.f;
     }
     if (lane_ok) {
-        u32x4 raw[kBlk][CPL];
-        bool use[kBlk];
-#pragma unroll
-        for (int j = 0; j < kBlk; ++j) {
-            const int t = tb + j;
-            use[j] = (t < n) && (p0 + t >= W);
-            const TIn *row = use[j] ? kv_row(Kbg, row_stride, ringK, t - W, n, p0, W, D) : nullptr;
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                raw[j][cc] = u32x4{0u, 0u, 0u, 0u};
-                if (row) raw[j][cc] = *reinterpret_cast<const u32x4 *>(row + (c0 + LPB * cc) * EPC);
-            }
-        }
 #pragma unroll
         for (int j = 0; j < kBlk; ++j) {
             if (!use[j]) continue;
@@ -171,8 +180,6 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
                 for (int e = 0; e < EPC; ++e) c16[(c0 + LPB * cc) * EPC + e] = Cs[cc][e];
         }
     }
-    __shared__ float blkv[4][4][D];  // [wave][block][d]
-    __shared__ float blkc[RM ? 4 : 1][4][RM ? D : 1];
     if (lane_ok) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
@@ -182,7 +189,6 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
                 if constexpr (RM) blkc[wave][blk][(c0 + LPB * cc) * EPC + e] = Cs[cc][e];
             }
     }
-    __shared__ float decay[4][4], beta[4][4];
     if (c0 == 0) {
         decay[wave][blk] = gl;
         beta[wave][blk] = bw;
@@ -213,6 +219,11 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
             for (int w = 0; w < 4; ++w) Bt = decay[wave][w] * Bt + beta[wave][w];
             a.beta64[trec] = Bt;
         }
+    }
+    // the next chain reuses this wave's LDS rows
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -949,13 +960,17 @@ template <typename TIn, typename TOut, int D>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t stream, int parts) {
     const unsigned tiles = (unsigned)(a.B * a.Hkv * a.ntiles);
     if (parts & kPrefillScan) {
-        const unsigned scan_tiles = (unsigned)(a.B * a.Hs * a.ntiles);
+        // one wave per (tile, b, KV head); per query head it feeds the group's chains
+        const unsigned scan_tiles = (unsigned)(a.B * a.Hkv * a.ntiles);
         const dim3 agg_grid((scan_tiles + 3) / 4), carry_grid(a.B * a.Hs * (D / kCarryCols));
         if (a.running_mean) {
-            hipLaunchKernelGGL((k_ewma_agg<TIn, D, true>), agg_grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_ewma_agg<TIn, D, true, false>), agg_grid, dim3(256), 0, stream, a);
             hipLaunchKernelGGL(k_ewma_carry<true>, carry_grid, dim3(1024), 0, stream, a);
         } else {
-            hipLaunchKernelGGL((k_ewma_agg<TIn, D, false>), agg_grid, dim3(256), 0, stream, a);
+            if (a.s_per_query)
+                hipLaunchKernelGGL((k_ewma_agg<TIn, D, false, true>), agg_grid, dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_ewma_agg<TIn, D, false, false>), agg_grid, dim3(256), 0, stream, a);
             hipLaunchKernelGGL(k_ewma_carry<false>, carry_grid, dim3(1024), 0, stream, a);
         }
     }

@@ -26,9 +26,10 @@
 //                  semantic sum as one MFMA contraction per 16-token group,
 //                  clip, scale, add, store.
 //   k_ring_out     last min(R, T) attention rows -> ring (after all reads).
-// Precision: the fp32 pool and the softmax weights enter the MFMAs as bf16
-// hi + lo pairs (x = hi + lo to ~2^-17 relative); bf16 attention values are
-// exact, fp32 attention values are split the same way.
+// Precision: the fp32 pool, the softmax weights and the band/field
+// coefficients enter the MFMAs as bf16 hi + lo pairs (x = hi + lo to ~2^-17
+// relative); bf16 attention values are exact, fp32 attention values are split
+// the same way (and pass through the epilogue from LDS, unsplit).
 #include <type_traits>
 
 #include "sfa_common.h"
@@ -39,7 +40,6 @@ namespace sfa {
 namespace {
 
 constexpr int kSlots = 64;
-constexpr int kCols = 64;          // columns per epilogue chunk (one per lane)
 constexpr int kOpElems = 64 * 8;   // one MFMA operand (64 lanes x 8 bf16)
 constexpr int kAggMaxH = 8192;     // hidden sizes whose field aggregate k_sem computes
 

@@ -357,6 +357,24 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // k_window_attn: windowed softmax attention + α·S epilogue
 // ---------------------------------------------------------------------------
+// One step of a log-step scan of S = A·S + V over the 16 lanes of a DPP row:
+// lane c16 takes the (A, V) of lane c16 - SH (row_shr; lanes below SH keep theirs)
+template <int SH>
+__device__ __forceinline__ float row_shr(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + SH, 0xf, 0xf, true));
+}
+template <int SH, int NK>
+__device__ __forceinline__ void row_scan_step(f32x4 (*V)[2], float &A, int c16) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) V[k][half][i] = fmaf(A, row_shr<SH>(V[k][half][i]), V[k][half][i]);
+    const float Ap = row_shr<SH>(A);
+    A = c16 >= SH ? A * Ap : A;
+}
+
 template <typename TIn> struct Lds;
 template <> struct Lds<__bf16> { static constexpr int kpad = 8, vpad = 0; };
 template <> struct Lds<float> { static constexpr int kpad = 4, vpad = 4; };
@@ -416,7 +434,11 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
 
     __shared__ __attribute__((aligned(16))) TIn Klds[kRows * KS];
     __shared__ __attribute__((aligned(16))) TIn Vt[D * VS];
-    __shared__ __attribute__((aligned(16))) float Sb[4][kBlk * SS];
+    // S per KV head with bf16 inputs stays in registers (epilogue layout, a row
+    // scan over the wave's 16 tokens); the LDS slot then only carries S at the
+    // block start.  The other modes keep each token's S row in LDS.
+    constexpr bool kRegS = !QH && !RM && kBf16;
+    __shared__ __attribute__((aligned(16))) float Sb[4][kRegS ? D : kBlk * SS];
 
     const int nblk = a.B * a.Hkv * a.ntiles;
     const int lid = xcd_remap(blockIdx.x, nblk);
@@ -630,6 +652,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
         }
     };
     float *Sw = Sb[wave];
+    f32x4 Sreg[kRegS ? D / 32 : 1][2];  // kRegS: S of the lane's token at d = 32k + 8q4 + 4half + i
     // QH: the keys evicted by this wave's 16 tokens, kept in registers (the K
     // staging area is reused in the head loop)
     float kev[QH ? kBlk : 1][EPL];
@@ -667,6 +690,44 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
         __syncthreads();
 
         // ---- (3) EWMA through the block: S_t after token t's own eviction -----
+        if constexpr (kRegS) {
+            // lane (q4, c16) needs S_t for its token t = tb + c16 at
+            // d = 32k + 8q4 + 4half + i.  Per token the step is S = A·S + V with
+            // (A, V) = (γ, (1-γ)·k_{t-W}) if t evicts, else (1, 0); a log-step
+            // scan over the 16 lanes of the row composes them, then
+            // S_t = A_{..t}·S_start + V_{..t}.
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) Sw[e0 + e] = S[e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int t = tb + c16;
+            const bool ev = t < n && p0 + t >= W;
+            float Ac = ev ? gm : 1.f;
+            const float w1 = ev ? 1.f - gm : 0.f;
+            // token t - W sits in staged row (t - W) - (t0 - 16)
+            const TIn *kr = &Klds[(kBlk * wave + c16 + kMaxWindow - W) * KS + 8 * q4];
+#pragma unroll
+            for (int k = 0; k < D / 32; ++k) {
+                const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(kr + 32 * k);
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Sreg[k][half][i] = w1 * (float)kk[4 * half + i];
+            }
+            row_scan_step<1, D / 32>(Sreg, Ac, c16);
+            row_scan_step<2, D / 32>(Sreg, Ac, c16);
+            row_scan_step<4, D / 32>(Sreg, Ac, c16);
+            row_scan_step<8, D / 32>(Sreg, Ac, c16);
+#pragma unroll
+            for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&Sw[32 * k + 8 * q4 + 4 * half]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Sreg[k][half][i] = fmaf(Ac, s0[i], Sreg[k][half][i]);
+                }
+        } else {
 #pragma unroll
         for (int j = 0; j < kBlk; ++j) {
             const int t = tb + j;
@@ -689,6 +750,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             }
 #pragma unroll
             for (int e = 0; e < EPL; ++e) Sw[j * SS + e0 + e] = S[e];
+        }
         }
     } else {
         __syncthreads();
@@ -834,7 +896,9 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
                         f32x4 o = {0.f, 0.f, 0.f, 0.f};
                         o = mfma_bf16_16x16x32(vop, Ph, o);
                         o = mfma_bf16_16x16x32(vop, Pl, o);
-                        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(Srow + 32 * k + 4 * half);
+                        f32x4 s4;
+                        if constexpr (kRegS) s4 = Sreg[k][half];
+                        else s4 = *reinterpret_cast<const f32x4 *>(Srow + 32 * k + 4 * half);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) ov[4 * half + i] = fmaf(al, s4[i], o[i]);
                     }

@@ -35,6 +35,12 @@
  *    window outside [1,16] or a too-small workspace returns
  *    SFA_ERR_INVALID_ARG; head_dim other than 64/128 or an unknown dtype
  *    returns SFA_ERR_UNSUPPORTED; a failed kernel launch returns SFA_ERR_HIP.
+ *    Sizes past the kernels' 32-bit tile and workgroup numbering also return
+ *    SFA_ERR_INVALID_ARG: prefill needs n <= 2^31 - 64 and
+ *    4 * B * Hs * ceil(n/64) < 2^31 (Hs: KV heads, query heads for the
+ *    per-query-head variant); decode needs 64 * L * B * Hkv < 2^31 and
+ *    128 * L * B * Hq < 2^31; the enhancement needs T <= 2^31 - 64 and
+ *    L * ceil(T/64) * ceil(H/128) < 2^31.
  *    On any error nothing has been written.  Zero-sized work (n == 0, B == 0,
  *    T == 0, L == 0) returns SFA_OK and enqueues nothing.
  *  - Thread safety: no global mutable state.  Concurrent calls are safe as long

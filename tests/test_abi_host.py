@@ -48,6 +48,8 @@ def test_workspace_sizes():
     assert lib.sfa_prefill_workspace_size(0, 10, 1, 64) == 0
     assert lib.sfa_enhance_workspace_size(24, 4096, 1024) > 0
     assert lib.sfa_enhance_workspace_size(1, 0, 1024) == 0
+    # tile counts in 64-bit arithmetic up to the largest int
+    assert lib.sfa_prefill_workspace_size(1, 2**31 - 1, 1, 64) == 2**25 * 64 * 4 * 6
 
 
 def _prefill(**kw):
@@ -85,6 +87,9 @@ INV, UNS, OK = _lib.SFA_ERR_INVALID_ARG, _lib.SFA_ERR_UNSUPPORTED, _lib.SFA_OK
     (dict(q=P + 2), INV), (dict(ring_v=None), INV), (dict(pos0=P, state=None), INV),
     (dict(pos0=P, ring_k=None, ring_v=None), INV),
     (dict(B=0, q=None, k=None, v=None), OK), (dict(n=0, q=None), OK),
+    # past the 32-bit tile numbering (with a workspace large enough not to be the reason)
+    (dict(n=2**31 - 10, ws_bytes=1 << 62), INV),
+    (dict(B=1 << 16, n=1 << 20, ws_bytes=1 << 62), INV),
 ])
 def test_prefill_rejects_before_launch(kw, want):
     assert _prefill(**kw) == want
@@ -94,6 +99,7 @@ def test_prefill_rejects_before_launch(kw, want):
     (dict(window=0), INV), (dict(Hq=5, Hkv=2), INV), (dict(d=32), UNS), (dict(in_dtype=3), UNS),
     (dict(pos=None), INV), (dict(state=None), INV), (dict(ring_k=P + 8), INV),
     (dict(L=0, q=None), OK), (dict(B=0, pos=None), OK),
+    (dict(L=1 << 13, B=1 << 12), INV),  # 64·L·B·Hkv reaches 2^31
 ])
 def test_decode_rejects_before_launch(kw, want):
     assert _decode(**kw) == want
@@ -105,6 +111,8 @@ def test_decode_rejects_before_launch(kw, want):
     (dict(H=96), UNS), (dict(n_layers=0), INV), (dict(layer0=1, n_layers=1), INV),
     (dict(stride=8), INV), (dict(pool=None), INV), (dict(ws_bytes=100), INV),
     (dict(T=0, attn=None), OK), (dict(L=0, attn=None), OK),
+    (dict(T=2**31 - 10, ws_bytes=1 << 62), INV),
+    (dict(L=1 << 13, n_layers=1 << 13, T=1 << 20, H=2048, ws_bytes=1 << 62), INV),
 ])
 def test_enhance_rejects_before_launch(kw, want):
     assert _enhance(**kw) == want

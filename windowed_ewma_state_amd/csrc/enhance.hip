@@ -884,7 +884,7 @@ hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
 }  // namespace
 
 size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers) {
-    const size_t nt = (size_t)((T + kTile - 1) / kTile);
+    const size_t nt = ((size_t)T + kTile - 1) / kTile;
     const size_t floats = 2 * (size_t)L * nt * H + (size_t)n_pool_layers * kSlots;
     // poolA and poolT: H/32 steps x 4 tiles (resp. H/16 x 2 steps) x hi/lo x 512 bf16
     const size_t ops = (size_t)n_pool_layers * (size_t)H * 64 * 2 * 2;

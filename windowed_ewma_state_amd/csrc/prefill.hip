@@ -1060,7 +1060,7 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t stream, int parts) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int B, int n, int Hkv, int d) {
-    const size_t nt = (size_t)((n + kTile - 1) / kTile);
+    const size_t nt = ((size_t)n + kTile - 1) / kTile;
     return (size_t)B * Hkv * nt * d * sizeof(float) * 6;
 }
 

@@ -3,6 +3,7 @@
 // Every entry point validates its arguments on the host before enqueuing
 // anything, then launches the kernels on the caller's stream.  The library
 // holds no global state, allocates nothing and never synchronises.
+#include <climits>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -57,6 +58,11 @@ int prefill_impl(int parts, int mode, const void *q, const void *k, const void *
     if (d != 64 && d != 128) return SFA_ERR_UNSUPPORTED;
     if ((ring_k == nullptr) != (ring_v == nullptr)) return SFA_ERR_INVALID_ARG;
     if (pos0 && (ring_k == nullptr || state == nullptr)) return SFA_ERR_INVALID_ARG;
+    if (n > INT_MAX - sfa::kTile) return SFA_ERR_INVALID_ARG;  // token indices of the last tile are 32-bit
+    {   // scan waves and attention workgroups are numbered with 32-bit integers
+        const long long chains = (long long)B * (mode == sfa::kQueryHead ? Hq : Hkv);
+        if (chains * ((n + sfa::kTile - 1) / sfa::kTile) * 4 >= (1LL << 31)) return SFA_ERR_INVALID_ARG;
+    }
     if (B == 0 || n == 0) return SFA_OK;
     if (!q || !k || !v || !gamma || !alpha || !out || !workspace) return SFA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -205,6 +211,10 @@ int sfa_enhance(const void *attn, void *out, float *ring, float *field, const fl
     if (!(temperature > 0.f) || !(clip >= 0.f) || pool_layer_stride < 0) return SFA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return SFA_ERR_UNSUPPORTED;
     if (H % 64 != 0) return SFA_ERR_UNSUPPORTED;
+    // token indices of the last tile and the workgroup numbers are 32-bit
+    if (T > INT_MAX - sfa::kTile) return SFA_ERR_INVALID_ARG;
+    if ((long long)L * ((T + sfa::kTile - 1) / sfa::kTile) * ((H + 127) / 128) >= (1LL << 31))
+        return SFA_ERR_INVALID_ARG;
     if (L == 0 || T == 0) return SFA_OK;
     if (!attn || !out || !ring || !field || !pool || !workspace) return SFA_ERR_INVALID_ARG;
     if (pool_layer_stride != 0 && pool_layer_stride < (long long)n_slots * H) return SFA_ERR_INVALID_ARG;

@@ -43,8 +43,10 @@
  *    L * ceil(T/64) * ceil(H/128) < 2^31.
  *    On any error nothing has been written.  Zero-sized work (n == 0, B == 0,
  *    T == 0, L == 0) returns SFA_OK and enqueues nothing.
- *  - Thread safety: no global mutable state.  Concurrent calls are safe as long
- *    as they do not share output, state or workspace buffers.
+ *  - Thread safety: the only global state is a per-device cache of how many
+ *    decode workgroups the device holds at once (an atomic, written once per
+ *    device with the value the runtime reports).  Concurrent calls are safe as
+ *    long as they do not share output, state or workspace buffers.
  */
 #ifndef SFA_H
 #define SFA_H

@@ -84,6 +84,26 @@ MUTANTS = {
                         "                if (e < -clip) e = -clip;\n                const double enh = e;"),
     "layer_ratio_over_L": ("(double)layer / (double)(n_layers - 1)", "(double)layer / (double)n_layers"),
     "decay_exponent_shifted": ("pow(cross_decay, (double)layer)", "pow(cross_decay, (double)(layer + 1))"),
+    "prefill_softmax_unnormalized": ("const double pj = sc[j - lo] / den;", "const double pj = sc[j - lo];"),
+    "prefill_pv_reads_keys": ("const double *vr = kv_row(v, ring_v, b, G, j, p0, n, Hkv, d, W, tv);",
+                              "const double *vr = kv_row(k, ring_k, b, G, j, p0, n, Hkv, d, W, tv);"),
+    "decode_softmax_unnormalized": ("o += (sc[j] / den) * rv[(size_t)j * d + e];",
+                                    "o += sc[j] * rv[(size_t)j * d + e];"),
+    "decode_pv_reads_keys": ("o += (sc[j] / den) * rv[(size_t)j * d + e];",
+                             "o += (sc[j] / den) * rk[(size_t)j * d + e];"),
+    "decode_query_of_group_head": ("const float *qr = q + (((size_t)l * B + b) * Hq + h) * d;",
+                                   "const float *qr = q + (((size_t)l * B + b) * Hq + G * group) * d;"),
+    "ring_never_written": ("for (int x = 0; x < H; ++x) R[(size_t)slot * H + x] = a[x];", "(void)slot;"),
+    "field_read_before_update": ("double e = rm + 0.5 * F[x] + 0.5 * sem;",
+                                 "double e = rm + 0.5 * (F[x] - (1.0 - ema_gamma) * a[x]) / ema_gamma + 0.5 * sem;"),
+    "semantic_unit_slots": ("sem += (c[i] / den) * (double)P[(size_t)i * H + x];",
+                            "sem += (c[i] / den) * (double)P[(size_t)i * H + x] / pn[i];"),
+    "cosine_without_slot_norm": ("c[i] = dot / (na * pn[i]) / temperature;", "c[i] = dot / na / temperature;"),
+    "slot_softmax_unnormalized": ("sem += (c[i] / den) * (double)P[(size_t)i * H + x];",
+                                  "sem += c[i] * (double)P[(size_t)i * H + x];"),
+    "enhancement_subtracted": ("out[((size_t)l * T + t) * H + x] = a[x] + enh;",
+                               "out[((size_t)l * T + t) * H + x] = a[x] - enh;"),
+    "clip_upper_only": ("                if (e < -clip) e = -clip;\n", ""),
 }
 
 

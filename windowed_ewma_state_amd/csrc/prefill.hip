@@ -771,7 +771,9 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             for (int w = 0; w < 3; ++w)
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) Ax[w][e] = Ain[w][e];
-            if (h + 1 < group) carry_loads(chain0 + h + 1, Cin, Ain);
+            // unconditional (the last head reloads its own carry), so that the
+            // waits for these loads are counted exactly
+            carry_loads(chain0 + min(h + 1, group - 1), Cin, Ain);
             block_start(gh, Cx, Ax, S);
 #pragma unroll
             for (int j = 0; j < kBlk; ++j) {

@@ -21,6 +21,9 @@
  *    asynchronous: results are valid once the stream reaches that point.
  *  - Layouts are dense and row-major.  "BNHD" = [batch, tokens, heads, head_dim]
  *    (the layout a fused QKV projection emits).
+ *  - Every tensor pointer and the workspace must be 16-byte aligned (the
+ *    kernels move 16-byte pieces); a misaligned one returns
+ *    SFA_ERR_INVALID_ARG.
  *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
  *  - S (the far-field state) is one fp32 d-vector per KV head; γ is per KV head,
  *    α per query head.
@@ -79,7 +82,7 @@ int sfa_abi_version(void);
 /*
  * Workspace bytes sfa_prefill needs for (B, n, Hkv, d): the chunked EWMA scan
  * keeps fp32 per-chunk aggregates and carries, proportional to B·Hkv·ceil(n/64)·d.
- * Returns 0 for zero-sized work.  Alignment of the workspace: 256 bytes.
+ * Returns 0 for zero-sized work.  The workspace must be 16-byte aligned.
  */
 size_t sfa_prefill_workspace_size(int B, int n, int Hkv, int d);
 
@@ -112,7 +115,7 @@ size_t sfa_prefill_workspace_size(int B, int n, int Hkv, int d);
  *           negative entries are treated as 0.
  *  window   W in [1,16]; scale <= 0 selects 1/sqrt(d).
  *  workspace, workspace_bytes: device scratch of at least
- *           sfa_prefill_workspace_size(B, n, Hkv, d) bytes, 256-byte aligned.
+ *           sfa_prefill_workspace_size(B, n, Hkv, d) bytes, 16-byte aligned.
  */
 int sfa_prefill(const void *q, const void *k, const void *v,
                 const float *gamma, const float *alpha,
@@ -243,7 +246,7 @@ int sfa_decode_step_rm(const void *q, const void *k_new, const void *v_new,
 
 /*
  * Workspace bytes sfa_enhance needs for (L, T, H): per-chunk fp32 aggregates
- * of the EMA field, proportional to L·ceil(T/64)·H.  256-byte aligned.
+ * of the EMA field, proportional to L·ceil(T/64)·H.  16-byte aligned.
  */
 size_t sfa_enhance_workspace_size(int L, int T, int H);
 

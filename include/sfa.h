@@ -7,7 +7,8 @@
  *   far field   S_t = γ·S_{t-1} + (1-γ)·k_evicted, where k_evicted is the key that
  *               leaves the window at step t (the key of position t-W);
  *   fusion      O = O_near + α·S_t.
- * Source: page "Signal Field Attention (SFA)：8KB代码实现4.16倍推理加速与248倍内存压缩",
+ * Source (the "first page" of the comments below): page
+ * "Signal Field Attention (SFA)：8KB代码实现4.16倍推理加速与248倍内存压缩",
  * section 2.1 (near-field, far-field and fusion equations) and section 2.2
  * (k = 16, constant O(k·d) memory).  The optional triple-channel enhancement
  * follows page "Dalin Soma SFA基于信号场注意力机制的神经网络推理加速框架"
@@ -152,8 +153,9 @@ int sfa_prefill_part(int parts, const void *q, const void *k, const void *v,
  * grouped-query attention: γ and the far-field state S belong to each QUERY
  * head.  Every query head of a group folds the same evicted keys (those of its
  * KV head) into its own S with its own decay; the near field and the ring are
- * those of sfa_prefill.  ([P1] §2.1 far-field and fusion equations; the
- * configs give "per-head γ" without saying which heads.)
+ * those of sfa_prefill.  (First page, section 2.1 far-field and fusion
+ * equations; under grouped-query attention a per-head γ can mean either kind
+ * of head.)
  *  gamma    [Hq] fp32.
  *  state    [B,Hq,d] fp32 (written; read first when pos0 != NULL).
  *  workspace at least sfa_prefill_workspace_size(B, n, Hq, d) bytes (the scan

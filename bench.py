@@ -375,6 +375,18 @@ def run_enhance(steps=20, warmup=3, sets=3):
 # ----------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on whole layers of the same workload
 # ----------------------------------------------------------------------------
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(n_layers, budget_s=10.0):
     import numpy as np
 
@@ -394,7 +406,8 @@ def cpu_baseline(n_layers, budget_s=10.0):
         if t_cpu >= budget_s:
             break
     return {"value": done * B * N * HQ / t_cpu, "unit": "tokens·heads/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": t_cpu,
+            "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": t_cpu,
             "sample": f"{done} of the 28 layers of the same 64K-token prefill workload, fp64 C oracle "
                       f"(OpenMP over heads), wall time of the oracle call only"}
 

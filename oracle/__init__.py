@@ -114,6 +114,8 @@ def prefill(q, k, v, gamma, alpha, window: int, scale: float = 0.0,
     Hkv = k.shape[2]
     assert k.shape == (B, n, Hkv, d) and v.shape == k.shape and Hq % Hkv == 0
     W = int(window)
+    if W < 1:
+        raise ValueError(f"window must be >= 1, got {W}")
     Hs = Hq if s_per_query else Hkv
     gamma = _np(np.broadcast_to(_np(gamma, np.float64), (Hs,)), np.float64)
     alpha = _np(np.broadcast_to(_np(alpha, np.float64), (Hq,)), np.float64)
@@ -150,6 +152,8 @@ def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha,
     rk = _np(ring_k, np.float64).copy()
     rv = _np(ring_v, np.float64).copy()
     W = rk.shape[3]
+    if W < 1:
+        raise ValueError(f"the ring needs at least one slot, got {W}")
     assert rk.shape == (L, B, Hkv, W, d) and rv.shape == rk.shape
     Hs = Hq if s_per_query else Hkv
     st = _np(state, np.float64).copy()

@@ -34,8 +34,19 @@
 #include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* A size the definitions do not cover stops the process with a message: the
+ * oracle never returns a result it did not compute. */
+static void require(int ok, const char *what) {
+    if (!ok) {
+        fprintf(stderr, "sfa oracle: invalid argument: %s\n", what);
+        fflush(stderr);
+        abort();
+    }
+}
 
 /* threads the OpenMP loops below use (reported with CPU timings) */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
@@ -99,6 +110,8 @@ void oracle_prefill(const float *q, const float *k, const float *v,
     const int group = Hq / Hkv;
     const int Hs = s_per_query ? Hq : Hkv; /* heads that own an S */
     const int sw = running_mean ? 2 * d : d; /* state words per S head */
+    require(B >= 0 && n >= 0 && d >= 1 && W >= 1 && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0,
+            "prefill sizes (W >= 1, Hq a multiple of Hkv)");
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
     /* final state of each (b, S head), written to state after the loop so that
      * every head reads the caller's ring/state as they were on entry */
@@ -225,8 +238,9 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                         double scale, int s_per_query, int running_mean) {
     const int group = Hq / Hkv;
     const int sw = running_mean ? 2 * d : d; /* state words per S head */
+    require(L >= 0 && B >= 0 && d >= 1 && W >= 1 && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0,
+            "decode sizes (W >= 1, Hq a multiple of Hkv)");
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
-    if (W > 64) return; /* the ring of [P1] §2.2 has k = 16 slots */
 
 #pragma omp parallel for collapse(3) schedule(dynamic)
     for (int l = 0; l < L; ++l) {
@@ -265,7 +279,7 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                 }
                 const int nvalid = (p >= W - 1) ? W : p + 1;
 
-                double sc[64];
+                double *sc = (double *)malloc(sizeof(double) * W);
                 for (int hh = 0; hh < group; ++hh) {
                     const int h = G * group + hh;
                     const float *qr = q + (((size_t)l * B + b) * Hq + h) * d;
@@ -287,6 +301,7 @@ void oracle_decode_step(const float *q, const float *k_new, const float *v_new,
                         dst[e] = o + a * S[e];
                     }
                 }
+                free(sc);
             }
         }
     }
@@ -324,6 +339,8 @@ void oracle_enhance(const float *attn, double *out, double *ring, double *field,
                     int L, int layer0, int n_layers, int T, int H, int t0,
                     double alpha_base, double cross_decay, double ema_gamma,
                     double temperature, double clip, int ring_size, int n_slots) {
+    require(L >= 0 && T >= 0 && H >= 1 && ring_size >= 1 && n_slots >= 1 && temperature > 0.0,
+            "enhance sizes (ring_size, n_slots >= 1, temperature > 0)");
 #pragma omp parallel for schedule(dynamic)
     for (int l = 0; l < L; ++l) {
         const double al = oracle_alpha_layer(alpha_base, cross_decay, layer0 + l, n_layers);

@@ -16,6 +16,8 @@ section 2.1 (near field, far field, fusion) and 2.2 (k = 16 ring);
 import json
 import math
 import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -23,6 +25,7 @@ import torch
 
 import oracle
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
 RNG = np.random.default_rng(20261203)
 
@@ -250,7 +253,7 @@ def test_brute_force_tiny(case):
 # P7 - P9: invariants
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("n,m,W", [(20, 5, 16), (3, 20, 16), (0, 9, 4), (16, 1, 16), (15, 2, 16),
-                                   (7, 7, 1)])
+                                   (7, 7, 1), (90, 12, 80)])
 def test_prefill_then_decode_equals_longer_prefill(n, m, W):
     """P7: prefill(n) followed by m decode steps reproduces prefill(n+m)."""
     B, Hq, Hkv, d = 2, 4, 2, 8
@@ -734,3 +737,22 @@ def test_decode_negative_position_skips_the_sequence():
                              pos[keep], gl, al)
     np.testing.assert_array_equal(out[:, keep], ref[0])
     np.testing.assert_array_equal(st2[:, keep], ref[3])
+
+
+def test_invalid_window_is_rejected_loudly():
+    """A window of zero slots is rejected by the wrapper, and the C library
+    itself aborts with a message instead of returning an unwritten result."""
+    q = _rand((1, 4, 1, 8))
+    with pytest.raises(ValueError):
+        oracle.prefill(q, q, q, 0.9, 0.1, 0)
+    with pytest.raises(ValueError):
+        oracle.decode_step(q[None, :, 0], q[None, :, 0], q[None, :, 0], np.zeros((1, 1, 1, 0, 8)),
+                           np.zeros((1, 1, 1, 0, 8)), np.zeros((1, 1, 1, 8)), np.zeros(1, np.int32),
+                           np.full((1, 1), 0.9), np.full((1, 1), 0.1))
+    code = ("import ctypes, numpy as np, oracle; L = oracle._load(); "
+            "z = np.zeros(64); "
+            "L.oracle_prefill(*[z.ctypes.data_as(ctypes.c_void_p)] * 9, None, "
+            "1, 4, 1, 1, 8, 0, 0.0, 0, 0)")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0 and "invalid argument" in r.stderr

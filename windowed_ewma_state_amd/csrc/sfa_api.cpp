@@ -2,7 +2,9 @@
 //
 // Every entry point validates its arguments on the host before enqueuing
 // anything, then launches the kernels on the caller's stream.  The library
-// holds no global state, allocates nothing and never synchronises.
+// allocates nothing and never synchronises.  Its only global state is a
+// per-device cache of the decode kernels' resident workgroup counts (atomics,
+// written once per device with the value the runtime reports).
 #include <climits>
 #include <hip/hip_runtime.h>
 #include <math.h>

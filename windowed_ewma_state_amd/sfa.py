@@ -7,6 +7,8 @@ stream.  Names and argument meanings follow the C entry points
 """
 from __future__ import annotations
 
+import functools
+
 import torch
 
 from . import _lib
@@ -43,6 +45,23 @@ def _stream(stream, device):
     return stream.cuda_stream
 
 
+def _on_call_stream(fn):
+    """Run an entry point with its stream (`stream=`, else the current one)
+    current.  The temporaries it allocates (a default workspace, γ/α converted
+    or broadcast to device vectors, default outputs and state) then belong to
+    that stream in the caching allocator: freed on return, they are not handed
+    to an allocation on another stream before the kernels enqueued on this one
+    have run."""
+    @functools.wraps(fn)
+    def wrapper(x, *args, stream=None, **kw):
+        if not isinstance(x, torch.Tensor) or not x.is_cuda:
+            raise TypeError(f"{fn.__name__}: the first argument must be a GPU tensor")
+        s = torch.cuda.current_stream(x.device) if stream is None else stream
+        with torch.cuda.stream(s):
+            return fn(x, *args, stream=s, **kw)
+    return wrapper
+
+
 def _vec(x, n, device, name):
     """Per-head parameter as an fp32 device vector of length n (scalars broadcast)."""
     if isinstance(x, torch.Tensor):
@@ -62,6 +81,7 @@ def prefill_workspace_size(B: int, n: int, Hkv: int, d: int) -> int:
     return int(_lib.lib().sfa_prefill_workspace_size(B, n, Hkv, d))
 
 
+@_on_call_stream
 def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=None,
             out_dtype=None, ring_k=None, ring_v=None, state=None, pos0=None, workspace=None,
             stream=None, parts: int | None = None, gamma_per_query_head: bool = False,
@@ -126,6 +146,7 @@ def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=
     return out, ring_k, ring_v, state
 
 
+@_on_call_stream
 def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, *, scale: float = 0.0,
                 out=None, out_dtype=None, stream=None, gamma_per_query_head: bool = False,
                 running_mean: bool = False):
@@ -170,6 +191,7 @@ def enhance_workspace_size(L: int, T: int, H: int) -> int:
     return int(_lib.lib().sfa_enhance_workspace_size(L, T, H))
 
 
+@_on_call_stream
 def enhance(attn, pool, ring, field, *, layer0: int = 0, n_layers: int | None = None, t0: int = 0,
             alpha_base: float = 0.1, cross_decay: float = 0.8, ema_gamma: float = 0.98,
             temperature: float = 0.07, clip: float = 0.5, shared_pool: bool = False, out=None,

@@ -47,10 +47,13 @@
  *    L * ceil(T/64) * ceil(H/128) < 2^31.
  *    On any error nothing has been written.  Zero-sized work (n == 0, B == 0,
  *    T == 0, L == 0) returns SFA_OK and enqueues nothing.
- *  - Thread safety: the only global state is a per-device cache of how many
- *    decode workgroups the device holds at once (an atomic, written once per
- *    device with the value the runtime reports).  Concurrent calls are safe as
- *    long as they do not share output, state or workspace buffers.
+ *  - Thread safety: the library's global state is a per-device cache of how
+ *    many decode workgroups the device holds at once (an atomic, written once
+ *    per device with the value the runtime reports) and, for
+ *    sfa_prefill_noalloc only, a static scratch array per device with a cache
+ *    of its address.  Concurrent calls are safe as long as they do not share
+ *    output, state or workspace buffers, and no two sfa_prefill_noalloc calls
+ *    overlap on one GPU.
  */
 #ifndef SFA_H
 #define SFA_H
@@ -66,7 +69,8 @@ enum {
     SFA_OK = 0,
     SFA_ERR_INVALID_ARG = 1,
     SFA_ERR_UNSUPPORTED = 2,
-    SFA_ERR_HIP = 3
+    SFA_ERR_HIP = 3,
+    SFA_ERR_TOO_LARGE = 4 /* sfa_prefill_noalloc: the call needs more than its static scratch */
 };
 
 enum { SFA_F32 = 0, SFA_BF16 = 1 };
@@ -190,6 +194,35 @@ int sfa_prefill_rm(const void *q, const void *k, const void *v,
                    int B, int n, int Hq, int Hkv, int d, int window, float scale,
                    int in_dtype, int out_dtype,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sfa_prefill_noalloc -- sfa_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace: the scan's per-chunk aggregates and
+ * carries go to a static device array of SFA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The call
+ * allocates and frees nothing (no hipMalloc, no allocating library routine);
+ * the caller still passes every input and output.
+ *
+ * Every argument, layout, result and error code is that of sfa_prefill, plus:
+ *  - SFA_ERR_TOO_LARGE (nothing enqueued or written) when
+ *    sfa_prefill_workspace_size(B, n, Hkv, d) > SFA_NOALLOC_SCRATCH_BYTES
+ *    (16 MiB: e.g. B·Hkv·ceil(n/64)·d up to 699,050 words of 24 bytes, which
+ *    holds one 65,536-token layer with 4 KV heads at head_dim 128);
+ *  - the scratch is shared by every call on the same GPU and keeps the last
+ *    call's contents (nothing in it needs to start at zero): calls that
+ *    overlap on one GPU (different streams, or threads without ordering) race
+ *    and must not be issued;
+ *  - the scratch address is looked up once per device, with the device that
+ *    owns `stream` current, on that device's first call.
+ */
+#define SFA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int sfa_prefill_noalloc(const void *q, const void *k, const void *v,
+                        const float *gamma, const float *alpha,
+                        void *out, void *ring_k, void *ring_v, float *state,
+                        const int32_t *pos0,
+                        int B, int n, int Hq, int Hkv, int d, int window, float scale,
+                        int in_dtype, int out_dtype, void *stream);
 
 /*
  * sfa_decode_step -- one generated token for L layers at once.

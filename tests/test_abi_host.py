@@ -34,8 +34,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib.lib()
-    assert lib.sfa_abi_version() == 1
-    for code in range(4):
+    assert lib.sfa_abi_version() == 2
+    for code in range(5):
         assert lib.sfa_status_string(code).startswith(b"SFA")
     assert b"unknown" in lib.sfa_status_string(99)
 
@@ -123,3 +123,29 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError, match="no CPU fallback"):
         _lib.lib()
+
+
+def _prefill_noalloc(**kw):
+    args = dict(q=P, k=P, v=P, gamma=P, alpha=P, out=P, ring_k=P, ring_v=P, state=P, pos0=None,
+                B=1, n=8, Hq=2, Hkv=1, d=64, window=16, scale=0.0, in_dtype=1, out_dtype=0,
+                stream=None)
+    args.update(kw)
+    return _lib.lib().sfa_prefill_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(window=0), INV), (dict(Hq=3, Hkv=2), INV), (dict(d=96), UNS), (dict(q=None), INV),
+    (dict(q=P + 2), INV), (dict(pos0=P, state=None), INV), (dict(B=0, q=None), OK),
+    # one 65,536-token layer with 4 KV heads at d 128 needs 12.6 MB: it fits;
+    # 4 of them need 50 MB: past the 16 MiB static scratch
+    (dict(B=4, n=65536, Hq=28, Hkv=4, d=128), _lib.SFA_ERR_TOO_LARGE),
+    (dict(B=1, n=200000, Hq=28, Hkv=4, d=128), _lib.SFA_ERR_TOO_LARGE),
+])
+def test_prefill_noalloc_rejects_before_launch(kw, want):
+    assert _prefill_noalloc(**kw) == want
+
+
+def test_prefill_noalloc_scratch_holds_the_64k_layer():
+    lib = _lib.lib()
+    assert lib.sfa_prefill_workspace_size(1, 65536, 4, 128) <= _lib.SFA_NOALLOC_SCRATCH_BYTES
+    assert b"TOO_LARGE" in lib.sfa_status_string(_lib.SFA_ERR_TOO_LARGE)

@@ -7,8 +7,8 @@ Hand-written HIP kernels behind a C ABI (include/sfa.h, libsfa.so):
 PyTorch supplies device memory and streams only.
 """
 from .sfa import (decode_step, enhance, enhance_workspace_size, prefill,  # noqa: F401
-                  prefill_workspace_size)
+                  prefill_noalloc, prefill_workspace_size)
 from ._lib import SFAError  # noqa: F401
 
-__all__ = ["prefill", "decode_step", "enhance", "prefill_workspace_size",
+__all__ = ["prefill", "prefill_noalloc", "decode_step", "enhance", "prefill_workspace_size",
            "enhance_workspace_size", "SFAError"]

@@ -11,13 +11,14 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsfa.so")
 
-SFA_OK, SFA_ERR_INVALID_ARG, SFA_ERR_UNSUPPORTED, SFA_ERR_HIP = 0, 1, 2, 3
+SFA_OK, SFA_ERR_INVALID_ARG, SFA_ERR_UNSUPPORTED, SFA_ERR_HIP, SFA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+SFA_NOALLOC_SCRATCH_BYTES = 16 << 20
 SFA_F32, SFA_BF16 = 0, 1
 SFA_PREFILL_SCAN, SFA_PREFILL_ATTEND = 1, 2
 
 # every symbol include/sfa.h declares
 EXPORTS = ("sfa_status_string", "sfa_abi_version", "sfa_prefill_workspace_size", "sfa_prefill",
-           "sfa_prefill_part", "sfa_prefill_qh", "sfa_prefill_rm",
+           "sfa_prefill_part", "sfa_prefill_qh", "sfa_prefill_rm", "sfa_prefill_noalloc",
            "sfa_decode_step", "sfa_decode_step_qh", "sfa_decode_step_rm", "sfa_enhance_workspace_size",
            "sfa_enhance")
 
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.sfa_prefill_qh.restype = I
         L.sfa_prefill_rm.argtypes = L.sfa_prefill.argtypes
         L.sfa_prefill_rm.restype = I
+        L.sfa_prefill_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
+        L.sfa_prefill_noalloc.restype = I
         L.sfa_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
         L.sfa_decode_step.restype = I
         L.sfa_decode_step_qh.argtypes = L.sfa_decode_step.argtypes

@@ -5,6 +5,7 @@
 // allocates nothing and never synchronises.  Its only global state is a
 // per-device cache of the decode kernels' resident workgroup counts (atomics,
 // written once per device with the value the runtime reports).
+#include <atomic>
 #include <climits>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -13,7 +14,41 @@
 #include "../../include/sfa.h"
 #include "sfa_internal.h"
 
+// ---- scratch of the no-allocation prefill (sfa_prefill_noalloc) -----------
+// One copy of this array per device, loaded with the library's code object
+// and held until the process ends.  In host code the name only stands in for
+// the symbol: every host use goes through the device's own address, looked up
+// once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SFA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+
+// device address of `scratch` on the device that owns `stream` (looked up with
+// that device current, once per device); NULL with *err set on failure
+void *scratch_for(hipStream_t stream, hipError_t *err) {
+    int dev = 0;
+    *err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxScratchDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    int cur = 0;
+    *err = hipGetDevice(&cur);
+    if (*err != hipSuccess) return nullptr;
+    if (cur != dev && (*err = hipSetDevice(dev)) != hipSuccess) return nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t restore = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (*err != hipSuccess) return nullptr;
+    if ((*err = restore) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool dtype_ok(int t) { return t == SFA_F32 || t == SFA_BF16; }
@@ -33,11 +68,14 @@ const char *sfa_status_string(int status) {
         case SFA_ERR_INVALID_ARG: return "SFA_ERR_INVALID_ARG: invalid argument";
         case SFA_ERR_UNSUPPORTED: return "SFA_ERR_UNSUPPORTED: unsupported head_dim, hidden size or dtype";
         case SFA_ERR_HIP: return "SFA_ERR_HIP: kernel launch failed";
+        case SFA_ERR_TOO_LARGE:
+            return "SFA_ERR_TOO_LARGE: the call needs more scratch than the no-allocation entry point's "
+                   "static buffer holds";
         default: return "SFA: unknown status";
     }
 }
 
-int sfa_abi_version(void) { return 1; }
+int sfa_abi_version(void) { return 2; }
 
 size_t sfa_prefill_workspace_size(int B, int n, int Hkv, int d) {
     if (B <= 0 || n <= 0 || Hkv <= 0 || d <= 0) return 0;
@@ -46,13 +84,14 @@ size_t sfa_prefill_workspace_size(int B, int n, int Hkv, int d) {
 
 namespace {
 
-// one prefill call; mode: sfa::kKvHead, kQueryHead (γ and S per query head,
-// Hs = Hq) or kRunningMean (state [B,Hkv,2,d], three times the workspace)
-int prefill_impl(int parts, int mode, const void *q, const void *k, const void *v,
-                 const float *gamma, const float *alpha, void *out, void *ring_k, void *ring_v,
-                 float *state, const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
-                 float scale, int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes,
-                 void *stream) {
+constexpr int kNothingToDo = -1;
+
+// argument checks of every prefill entry point except those of the workspace:
+// SFA_OK, an error code, or kNothingToDo for zero-sized work
+int prefill_check(int parts, int mode, const void *q, const void *k, const void *v,
+                  const float *gamma, const float *alpha, void *out, void *ring_k, void *ring_v,
+                  float *state, const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
+                  int in_dtype, int out_dtype) {
     if (parts < 1 || parts > (SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND)) return SFA_ERR_INVALID_ARG;
     if (B < 0 || n < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return SFA_ERR_INVALID_ARG;
     if (window < 1 || window > SFA_MAX_WINDOW) return SFA_ERR_INVALID_ARG;
@@ -65,16 +104,35 @@ int prefill_impl(int parts, int mode, const void *q, const void *k, const void *
         const long long chains = (long long)B * (mode == sfa::kQueryHead ? Hq : Hkv);
         if (chains * ((n + sfa::kTile - 1) / sfa::kTile) * 4 >= (1LL << 31)) return SFA_ERR_INVALID_ARG;
     }
-    if (B == 0 || n == 0) return SFA_OK;
-    if (!q || !k || !v || !gamma || !alpha || !out || !workspace) return SFA_ERR_INVALID_ARG;
+    if (B == 0 || n == 0) return kNothingToDo;
+    if (!q || !k || !v || !gamma || !alpha || !out) return SFA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        (ring_k && (!aligned(ring_k, 16) || !aligned(ring_v, 16))) || (state && !aligned(state, 16)) ||
-        !aligned(workspace, 16))
+        (ring_k && (!aligned(ring_k, 16) || !aligned(ring_v, 16))) || (state && !aligned(state, 16)))
         return SFA_ERR_INVALID_ARG;
+    return SFA_OK;
+}
+
+// workspace bytes of a prefill call in this mode (sizes already checked)
+size_t prefill_need(int mode, int B, int n, int Hq, int Hkv, int d) {
+    const int chains = mode == sfa::kQueryHead ? Hq : mode == sfa::kRunningMean ? 3 * Hkv : Hkv;
+    return sfa::prefill_workspace_bytes(B, n, chains, d);
+}
+
+// one prefill call; mode: sfa::kKvHead, kQueryHead (γ and S per query head,
+// Hs = Hq) or kRunningMean (state [B,Hkv,2,d], three times the workspace)
+int prefill_impl(int parts, int mode, const void *q, const void *k, const void *v,
+                 const float *gamma, const float *alpha, void *out, void *ring_k, void *ring_v,
+                 float *state, const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
+                 float scale, int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+    const int chk = prefill_check(parts, mode, q, k, v, gamma, alpha, out, ring_k, ring_v, state, pos0, B,
+                                  n, Hq, Hkv, d, window, in_dtype, out_dtype);
+    if (chk == kNothingToDo) return SFA_OK;
+    if (chk != SFA_OK) return chk;
+    if (!workspace || !aligned(workspace, 16)) return SFA_ERR_INVALID_ARG;
+    if (workspace_bytes < prefill_need(mode, B, n, Hq, Hkv, d)) return SFA_ERR_INVALID_ARG;
     const int s_per_query = mode == sfa::kQueryHead, running_mean = mode == sfa::kRunningMean;
     const int Hs = s_per_query ? Hq : Hkv;
-    if (workspace_bytes < sfa::prefill_workspace_bytes(B, n, running_mean ? 3 * Hkv : Hs, d))
-        return SFA_ERR_INVALID_ARG;
 
     sfa::PrefillArgs a;
     a.q = q; a.k = k; a.v = v;
@@ -170,6 +228,24 @@ int sfa_prefill_rm(const void *q, const void *k, const void *v, const float *gam
     return prefill_impl(SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND, sfa::kRunningMean, q, k, v, gamma, alpha,
                         out, ring_k, ring_v, state, pos0, B, n, Hq, Hkv, d, window, scale, in_dtype,
                         out_dtype, workspace, workspace_bytes, stream);
+}
+
+int sfa_prefill_noalloc(const void *q, const void *k, const void *v, const float *gamma,
+                        const float *alpha, void *out, void *ring_k, void *ring_v, float *state,
+                        const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
+                        float scale, int in_dtype, int out_dtype, void *stream) {
+    const int parts = SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND;
+    const int chk = prefill_check(parts, sfa::kKvHead, q, k, v, gamma, alpha, out, ring_k, ring_v, state,
+                                  pos0, B, n, Hq, Hkv, d, window, in_dtype, out_dtype);
+    if (chk == kNothingToDo) return SFA_OK;
+    if (chk != SFA_OK) return chk;
+    if (prefill_need(sfa::kKvHead, B, n, Hq, Hkv, d) > SFA_NOALLOC_SCRATCH_BYTES) return SFA_ERR_TOO_LARGE;
+    hipError_t err = hipSuccess;
+    void *ws = scratch_for(static_cast<hipStream_t>(stream), &err);
+    if (!ws) return SFA_ERR_HIP;
+    return prefill_impl(parts, sfa::kKvHead, q, k, v, gamma, alpha, out, ring_k, ring_v, state, pos0, B, n,
+                        Hq, Hkv, d, window, scale, in_dtype, out_dtype, ws, SFA_NOALLOC_SCRATCH_BYTES,
+                        stream);
 }
 
 int sfa_decode_step(const void *q, const void *k_new, const void *v_new, void *ring_k, void *ring_v,

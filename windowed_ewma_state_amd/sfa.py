@@ -147,6 +147,35 @@ def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=
 
 
 @_on_call_stream
+def prefill_noalloc(q, k, v, gamma, alpha, *, out, ring_k, ring_v, state, pos0=None, window: int = 16,
+                    scale: float = 0.0, stream=None):
+    """sfa_prefill_noalloc: sfa_prefill with the library's static scratch as the
+    workspace, for callers that cannot allocate.  Nothing is allocated here
+    either: every buffer is the caller's (gamma [Hkv] and alpha [Hq] as fp32
+    device tensors, out [B,n,Hq,d], ring_k/ring_v [B,Hkv,W,d], state [B,Hkv,d]
+    fp32, pos0 [B] int32 or None).  Calls that overlap on one GPU race."""
+    B, n, Hq, d = q.shape
+    Hkv = k.shape[2]
+    dev = q.device
+    W = int(window)
+    for t, name in ((out, "out"), (ring_k, "ring_k"), (ring_v, "ring_v"), (state, "state")):
+        if t is None:
+            raise ValueError(f"sfa_prefill_noalloc allocates nothing: pass {name}")
+    st = _lib.lib().sfa_prefill_noalloc(
+        _dev(q, "q", q.dtype, (B, n, Hq, d), dev), _dev(k, "k", q.dtype, (B, n, Hkv, d), dev),
+        _dev(v, "v", q.dtype, (B, n, Hkv, d), dev), _dev(gamma, "gamma", torch.float32, (Hkv,), dev),
+        _dev(alpha, "alpha", torch.float32, (Hq,), dev), _dev(out, "out", None, (B, n, Hq, d), dev),
+        _dev(ring_k, "ring_k", q.dtype, (B, Hkv, W, d), dev),
+        _dev(ring_v, "ring_v", q.dtype, (B, Hkv, W, d), dev),
+        _dev(state, "state", torch.float32, (B, Hkv, d), dev),
+        _dev(pos0, "pos0", torch.int32, (B,), dev),
+        B, n, Hq, Hkv, d, W, float(scale), _dtype_code(q, "q"), _dtype_code(out, "out"),
+        _stream(stream, dev))
+    _lib.check(st, "sfa_prefill_noalloc")
+    return out, ring_k, ring_v, state
+
+
+@_on_call_stream
 def decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, *, scale: float = 0.0,
                 out=None, out_dtype=None, stream=None, gamma_per_query_head: bool = False,
                 running_mean: bool = False):

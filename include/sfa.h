@@ -280,8 +280,10 @@ int sfa_decode_step_rm(const void *q, const void *k_new, const void *v_new,
                        int in_dtype, int out_dtype, void *stream);
 
 /*
- * Workspace bytes sfa_enhance needs for (L, T, H): per-chunk fp32 aggregates
- * of the EMA field, proportional to L·ceil(T/64)·H.  16-byte aligned.
+ * Workspace bytes sfa_enhance (and sfa_enhance_prepared) needs for (L, T, H):
+ * per-chunk fp32 aggregates of the EMA field, proportional to L·ceil(T/64)·H,
+ * the carried ring, the slot weights of every 64-token chunk and, for
+ * sfa_enhance, the pool's MFMA operands.  16-byte aligned.
  */
 size_t sfa_enhance_workspace_size(int L, int T, int H);
 
@@ -319,6 +321,43 @@ int sfa_enhance(const void *attn, void *out, float *ring, float *field,
                 float clip, int ring_size, int n_slots,
                 int in_dtype, int out_dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The semantic pool is read-only ("Dalin Soma SFA..." section 2.1: a fixed set
+ * of 64 slots), so the MFMA operands sfa_enhance derives from it on every call
+ * (the slots split into bf16 hi + lo in the two operand orders, 1/|slot| and
+ * the largest |element| of every slot) can be derived once and kept:
+ *
+ * sfa_enhance_pool_bytes -- bytes of the prepared form of n_pool_layers pool
+ *   layers at hidden size H: one record of sfa_enhance_pool_bytes(1, H) bytes
+ *   (a multiple of 256) per layer, in layer order.
+ *
+ * sfa_enhance_prepare_pool -- writes the prepared form of pool layers
+ *   0..n_pool_layers-1 (layer j at pool + j·pool_layer_stride floats, each
+ *   [n_slots, H] fp32, as in sfa_enhance) into `prepared` (device memory of at
+ *   least sfa_enhance_pool_bytes(n_pool_layers, H) bytes, 256-byte aligned,
+ *   owned by the caller).  Asynchronous on `stream`; the pool is only read.
+ *   n_slots in [1,64], H a multiple of 64 (else SFA_ERR_UNSUPPORTED),
+ *   pool_layer_stride >= n_slots·H when n_pool_layers > 1.
+ *
+ * sfa_enhance_prepared -- sfa_enhance with the pool given in prepared form:
+ *   with shared_pool != 0 every layer of the call uses record 0 of
+ *   `prepared`; otherwise layer i of the call uses record i (for a call that
+ *   starts at global layer layer0, pass prepared + layer0·sfa_enhance_pool_bytes(1, H)
+ *   when the records are kept for every layer of the model).  n_slots must be
+ *   the value the records were prepared with.  Every other argument, result
+ *   and error code is that of sfa_enhance; the workspace is the same size.
+ */
+size_t sfa_enhance_pool_bytes(int n_pool_layers, int H);
+int sfa_enhance_prepare_pool(const float *pool, long long pool_layer_stride, int n_pool_layers,
+                             int n_slots, int H, void *prepared, size_t prepared_bytes, void *stream);
+int sfa_enhance_prepared(const void *attn, void *out, float *ring, float *field,
+                         const void *prepared, int shared_pool, float *enhancement,
+                         int L, int layer0, int n_layers, int T, int H, int t0,
+                         float alpha_base, float cross_decay, float ema_gamma, float temperature,
+                         float clip, int ring_size, int n_slots,
+                         int in_dtype, int out_dtype,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -149,3 +149,45 @@ def test_prefill_noalloc_scratch_holds_the_64k_layer():
     lib = _lib.lib()
     assert lib.sfa_prefill_workspace_size(1, 65536, 4, 128) <= _lib.SFA_NOALLOC_SCRATCH_BYTES
     assert b"TOO_LARGE" in lib.sfa_status_string(_lib.SFA_ERR_TOO_LARGE)
+
+
+def _prepare_pool(**kw):
+    args = dict(pool=P, stride=0, n_pool_layers=1, n_slots=64, H=64, prepared=P, prepared_bytes=1 << 20,
+                stream=None)
+    args.update(kw)
+    return _lib.lib().sfa_enhance_prepare_pool(*args.values())
+
+
+def _enhance_prepared(**kw):
+    args = dict(attn=P, out=P, ring=P, field=P, prepared=P, shared=1, enh=None, L=1, layer0=0,
+                n_layers=1, T=8, H=64, t0=0, alpha_base=0.1, cross_decay=0.8, ema_gamma=0.98,
+                temperature=0.07, clip=0.5, ring_size=16, n_slots=64, in_dtype=1, out_dtype=1,
+                ws=P, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return _lib.lib().sfa_enhance_prepared(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n_slots=0), INV), (dict(n_slots=65), INV), (dict(H=96), UNS), (dict(pool=None), INV),
+    (dict(prepared=None), INV), (dict(prepared=P + 16), INV), (dict(prepared_bytes=100), INV),
+    (dict(n_pool_layers=2, stride=64), INV), (dict(stride=-4), INV), (dict(n_pool_layers=0, pool=None), OK),
+])
+def test_enhance_prepare_pool_rejects_before_launch(kw, want):
+    assert _prepare_pool(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(ring_size=0), INV), (dict(n_slots=65), INV), (dict(H=96), UNS), (dict(prepared=None), INV),
+    (dict(prepared=P + 16), INV), (dict(ws=None), INV), (dict(ws_bytes=100), INV),
+    (dict(layer0=1, n_layers=1), INV), (dict(T=0, attn=None), OK),
+])
+def test_enhance_prepared_rejects_before_launch(kw, want):
+    assert _enhance_prepared(**kw) == want
+
+
+def test_enhance_pool_bytes():
+    lib = _lib.lib()
+    rec = lib.sfa_enhance_pool_bytes(1, 1024)
+    assert rec % 256 == 0 and rec >= 1024 * 64 * 4 * 2  # both operand orders, bf16 hi + lo
+    assert lib.sfa_enhance_pool_bytes(24, 1024) == 24 * rec
+    assert lib.sfa_enhance_pool_bytes(0, 1024) == 0

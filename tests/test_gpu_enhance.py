@@ -137,3 +137,38 @@ def test_enhance_alpha_zero_is_identity_on_gpu():
                           torch.bfloat16, alpha_base=0.0)
     assert torch.equal(out.cpu(), d["attn"])
     assert torch.all(enh == 0)
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["per-layer", "shared"])
+def test_enhance_prepared_pool_equals_per_call(shared):
+    """sfa_enhance_prepared on a pool prepared once == sfa_enhance (bit for bit),
+    two calls in a row continuing the stream, the second starting at global
+    layer 2 of 5 (records from layer 2 on); and both against the oracle."""
+    L, T, H, S = 3, 150, 256, 64
+    log(f"enhance prepared pool, shared={shared}")
+    d = inputs.enhance_inputs(5, T, H, seed=88, n_slots=S)
+    pool_all = d["pool"][0].contiguous() if shared else d["pool"].contiguous()
+    prep = sfa.enhance_prepare_pool(pool_all.cuda(), shared_pool=shared)
+    kw = dict(alpha_base=0.5, cross_decay=0.9, ema_gamma=0.95, temperature=0.07, clip=0.5)
+    attn = d["attn"][2:2 + L].contiguous()
+    pool = pool_all if shared else pool_all[2:2 + L].contiguous()
+    ring0 = torch.zeros((L, 16, H), device="cuda")
+    field0 = torch.zeros((L, H), device="cuda")
+    g1, g2 = (ring0.clone(), field0.clone()), (ring0.clone(), field0.clone())
+    outs = []
+    for t0, sl in ((0, slice(0, 100)), (100, slice(100, T))):
+        a = attn[:, sl].contiguous().cuda()
+        e1 = torch.empty(a.shape, device="cuda")
+        e2 = torch.empty(a.shape, device="cuda")
+        o1, _ = sfa.enhance(a, pool.cuda(), *g1, layer0=2, n_layers=5, t0=t0, shared_pool=shared,
+                            out_dtype=torch.float32, enhancement=e1, **kw)
+        o2, _ = sfa.enhance_prepared(a, prep.layer_offset(2), *g2, layer0=2, n_layers=5, t0=t0,
+                                     out_dtype=torch.float32, enhancement=e2, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(e1, e2)
+        assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
+        outs.append((o2, e2))
+    ref = oracle.enhance(attn, pool, shared_pool=shared, layer0=2, n_layers=5, ring_size=16, **kw)
+    check_output(torch.cat([o for o, _ in outs], 1), ref[0], True, "out")
+    _check_elementwise(torch.cat([e for _, e in outs], 1), ref[1], dict(layer0=2, n_layers=5, **kw))
+    check_exact(g2[0], ref[2], "ring")

@@ -20,7 +20,7 @@ SFA_PREFILL_SCAN, SFA_PREFILL_ATTEND = 1, 2
 EXPORTS = ("sfa_status_string", "sfa_abi_version", "sfa_prefill_workspace_size", "sfa_prefill",
            "sfa_prefill_part", "sfa_prefill_qh", "sfa_prefill_rm", "sfa_prefill_noalloc",
            "sfa_decode_step", "sfa_decode_step_qh", "sfa_decode_step_rm", "sfa_enhance_workspace_size",
-           "sfa_enhance")
+           "sfa_enhance", "sfa_enhance_pool_bytes", "sfa_enhance_prepare_pool", "sfa_enhance_prepared")
 
 _lib = None
 
@@ -68,6 +68,13 @@ def lib() -> ctypes.CDLL:
         L.sfa_enhance.argtypes = [P, P, P, P, P, ctypes.c_longlong, P, I, I, I, I, I, I,
                                   F, F, F, F, F, I, I, I, I, P, Z, P]
         L.sfa_enhance.restype = I
+        L.sfa_enhance_pool_bytes.argtypes = [I, I]
+        L.sfa_enhance_pool_bytes.restype = Z
+        L.sfa_enhance_prepare_pool.argtypes = [P, ctypes.c_longlong, I, I, I, P, Z, P]
+        L.sfa_enhance_prepare_pool.restype = I
+        L.sfa_enhance_prepared.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I,
+                                           F, F, F, F, F, I, I, I, I, P, Z, P]
+        L.sfa_enhance_prepared.restype = I
         _lib = L
     return _lib
 

@@ -12,20 +12,24 @@
 // slots, clip 0.5) are the SFA_Config of page "Signal Field Attention (SFA)".
 //
 // Launches:
-//   k_prep         pool -> bf16 hi/lo in the two MFMA operand orders; 1/|s| of
-//                  every pool slot; the band/field operands; α of each layer.
+//   k_pool_prep    pool -> bf16 hi/lo in the two MFMA operand orders, 1/|s| and
+//                  max |s[x]| of every slot: one record per pool layer.  Run per
+//                  call by sfa_enhance, once by sfa_enhance_prepare_pool (the
+//                  pool is read-only, so its records can be kept).
 //   k_field_agg    EMA of each 64-token tile from zero (a thread per 16-byte
 //                  column chunk); only for hidden sizes above kAggMaxH.
 //   k_sem          one workgroup per (layer, 64-token tile): cosine scores
 //                  C^T = pool · a^T (MFMA), softmax over the slots, 0.5·weights
 //                  as MFMA operands in the workspace; on the same pass over
-//                  the tile, its field aggregate (EMA from zero).
-//   k_field_carry  field before each tile (exclusive scan), final field.
+//                  the tile, its field aggregate (EMA from zero).  Extra
+//                  workgroups copy the carried ring to the workspace.
+//   k_field_carry  field before each tile (exclusive scan), final field; extra
+//                  workgroups write the band/field operand table, α of each
+//                  layer and the new ring (the last min(R, T) attention rows).
 //   k_cols         one workgroup per (layer, 64-token tile, 128 columns): the
 //                  tile staged column-major in LDS; ring mean, field and the
 //                  semantic sum as one MFMA contraction per 16-token group,
 //                  clip, scale, add, store.
-//   k_ring_out     last min(R, T) attention rows -> ring (after all reads).
 // Precision: the fp32 pool, the softmax weights and the band/field
 // coefficients enter the MFMAs as bf16 hi + lo pairs (x = hi + lo to ~2^-17
 // relative); bf16 attention values are exact, fp32 attention values are split
@@ -42,6 +46,10 @@ namespace {
 constexpr int kSlots = 64;
 constexpr int kOpElems = 64 * 8;   // one MFMA operand (64 lanes x 8 bf16)
 constexpr int kAggMaxH = 8192;     // hidden sizes whose field aggregate k_sem computes
+constexpr int kCoefEnt = 8;        // (token group, k-step) pairs of the band/field operand
+constexpr int kTabEntries = kCoefEnt * 2 * 64;  // band/field operands (u32x4)
+// workgroups that write the band/field operand table and α of each layer
+__host__ __device__ inline int kCallTableBlocks(const EnhanceArgs &a) { return kTabEntries / 256 + (a.L + 255) / 256; }
 
 // sum over the 16 lanes of a DPP row (every lane of the row gets it)
 __device__ __forceinline__ float row_sum16(float v) {
@@ -76,8 +84,19 @@ __device__ __forceinline__ bf16x8 get8(const uint16_t *src) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src));
 }
 
+// the prepared record of pool layer pl: slot norms, then the two operand tables
+__device__ __forceinline__ unsigned char *pool_rec(const EnhanceArgs &a, int pl) {
+    return a.pool_rec + (long long)pl * a.pool_rec_bytes;
+}
+__device__ __forceinline__ uint16_t *rec_poolA(const EnhanceArgs &a, int pl) {
+    return reinterpret_cast<uint16_t *>(pool_rec(a, pl) + kPoolRecHeader);
+}
+__device__ __forceinline__ uint16_t *rec_poolT(const EnhanceArgs &a, int pl) {
+    return rec_poolA(a, pl) + (long)a.H * 128;
+}
+
 // ---------------------------------------------------------------------------
-// Pool operands (the first workgroups of k_prep).  Per pool layer pl:
+// Pool operands (the first workgroups of k_pool_prep).  Per pool layer pl:
 //   poolA[pl][ks][j][hl][lane][8]: slot 16j + lane%16, x = 32ks + 8(lane/16) + e
 //       (A operand of the cosine scores, k = hidden dim)
 //   poolT[pl][xg][ks][hl][lane][8]: x = 16xg + lane%16,
@@ -91,8 +110,8 @@ __device__ __forceinline__ void pool_prep_block(const EnhanceArgs &a, int bid) {
     const float *P = a.pool + (long)pl * a.pool_stride;
     const int j = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int q4 = lane / 16, c16 = lane % 16;
-    uint16_t *poolA = a.poolA + (long)pl * ksteps * 4 * 2 * kOpElems;
-    uint16_t *poolT = a.poolT + (long)pl * (a.H / 16) * 2 * 2 * kOpElems;
+    uint16_t *poolA = rec_poolA(a, pl);
+    uint16_t *poolT = rec_poolT(a, pl);
     uint16_t hi[8], lo[8];
     {   // cosine operand
         const int slot = 16 * j + c16;
@@ -188,9 +207,20 @@ __global__ __launch_bounds__(256) void k_field_agg(EnhanceArgs a) {
 // writes the field before each of its tiles.
 // ---------------------------------------------------------------------------
 constexpr int kFcParts = 8, kFcCols = 32;
+__device__ void call_tables_block(const EnhanceArgs &a, int bid);
+template <typename TIn>
+__device__ void ring_write_block(const EnhanceArgs &a, int bid);
+
+template <typename TIn>
 __global__ __launch_bounds__(256) void k_field_carry(EnhanceArgs a) {
     __shared__ float pX[kFcParts][kFcCols], pG[kFcParts];
     const int cpb = a.H / kFcCols;
+    {   // past the carry workgroups: the call's operand table and α, then the new ring
+        const int extra = (int)blockIdx.x - a.L * cpb;
+        const int ntab = kCallTableBlocks(a);
+        if (extra >= ntab) return ring_write_block<TIn>(a, extra - ntab);
+        if (extra >= 0) return call_tables_block(a, extra);
+    }
     const int l = blockIdx.x / cpb;
     const int col = threadIdx.x % kFcCols, part = threadIdx.x / kFcCols;
     const int x = (blockIdx.x % cpb) * kFcCols + col;
@@ -261,8 +291,18 @@ __device__ __forceinline__ void split_a8<float>(const u32x4 *w, bf16x8 &hi, bf16
     }
 }
 
+// copy of the carried ring (row bid of [L][R]) into the workspace: k_cols
+// reads the band's tokens before the call from there, so the ring itself can
+// be rewritten before k_cols runs
+__device__ __forceinline__ void halo_copy_block(const EnhanceArgs &a, int bid) {
+    const float4 *src = reinterpret_cast<const float4 *>(a.ring + (long)bid * a.H);
+    float4 *dst = reinterpret_cast<float4 *>(a.halo + (long)bid * a.H);
+    for (int x = threadIdx.x; x < a.H / 4; x += 256) dst[x] = src[x];
+}
+
 template <typename TIn>
 __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
+    if ((int)blockIdx.x >= a.L * a.ntiles) return halo_copy_block(a, blockIdx.x - a.L * a.ntiles);
     constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split a as well
     struct Phase1 {
         f32x4 cp[4][2][4][64];  // [wave][slot tile in round][token group][lane]
@@ -279,10 +319,10 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
     const int q4 = lane >> 4, c16 = lane & 15;
     const int H = a.H, T = a.T;
     const int tb = tile * kTile;
-    const int pl = a.pool_stride == 0 ? 0 : l;
+    const int pl = a.n_pool_layers == 1 ? 0 : l;
     const int ksteps = H / 32;
-    const uint16_t *poolA = a.poolA + (long)pl * ksteps * 4 * 2 * kOpElems + lane * 8;
-    const float *sinv = a.slot_norm + pl * kSlots;  // 1 / |s| per slot
+    const uint16_t *poolA = rec_poolA(a, pl) + lane * 8;
+    const float *sinv = reinterpret_cast<const float *>(pool_rec(a, pl));  // 1 / |s| per slot
     const TIn *Ag = reinterpret_cast<const TIn *>(a.attn) + (long)l * T * H;
     const int nj = (a.n_slots + 15) / 16;
     // B operands of this wave's token group, [ks][hi/lo][lane][8]
@@ -488,8 +528,6 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
 // the outputs leave through LDS as whole rows (full 128-byte lines).
 // ---------------------------------------------------------------------------
 constexpr int kCB = 128;       // columns per workgroup
-constexpr int kCoefEnt = 8;    // (token group, k-step) pairs of the band/field operand
-constexpr int kTabEntries = kCoefEnt * 2 * 64;  // band/field operands (u32x4)
 // token group tg uses the k-steps s = 0 .. kSteps[tg]-1 (staged rows 32s .. 32s+31),
 // table entries {0, 1, 3, 5}[tg] + s; its own tokens sit in k-step kIdStep[tg]
 
@@ -573,8 +611,8 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     u32x4 tab[NTAB / 256];
 #pragma unroll
     for (int k = 0; k < NTAB / 256; ++k) tab[k] = reinterpret_cast<const u32x4 *>(a.coef)[threadIdx.x + 256 * k];
-    const int pl = a.pool_stride == 0 ? 0 : l;
-    const uint16_t *poolT = a.poolT + (long)pl * (H / 16) * 2 * 2 * kOpElems + lane * 8;
+    const int pl = a.n_pool_layers == 1 ? 0 : l;
+    const uint16_t *poolT = rec_poolT(a, pl) + lane * 8;
     constexpr int SL = 2;  // the semantic operands as bf16 hi + lo
     bf16x8 pt[2][2][SL];  // [half][slot k-step][hi/lo]
     float Fc[8];
@@ -669,7 +707,7 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
         const float invR = 1.f / (float)R;
         const float al = load_uniform(a.alpha_tab + l);  // α of this layer
         const float gc = powi(g, c16 + 1), g16 = powi(g, kBlk);
-        const float *ringl = a.ring + (long)l * R * H;
+        const float *ringl = a.halo + (long)l * R * H;  // the ring as it was before the call
         const int ring0 = a.t0 % R;  // slot of relative token 0
         float *Eg = a.enhancement ? a.enhancement + (long)l * T * H : nullptr;
 #pragma unroll
@@ -749,7 +787,7 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int h = k >> 2, i = k & 3;
-                const float e = fminf(fmaxf(D[h][i], -a.clip), a.clip);
+                const float e = __builtin_amdgcn_fmed3f(D[h][i], -a.clip, a.clip);  // clip (clip >= 0)
                 en[k] = al * e;
                 float av;
                 if constexpr (kPrecise) {
@@ -801,10 +839,10 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
 }
 
 // last min(R, T) attention rows -> ring slots (t0 + t) mod R; one workgroup
-// per (layer, row)
+// per (layer, row).  Runs after the carried ring was copied to the workspace.
 template <typename TIn>
-__global__ __launch_bounds__(256) void k_ring_out(EnhanceArgs a) {
-    const int l = blockIdx.x / a.R, r = blockIdx.x % a.R;
+__device__ void ring_write_block(const EnhanceArgs &a, int bid) {
+    const int l = bid / a.R, r = bid % a.R;
     const int first = max(0, a.T - a.R);
     const int t = first + r;
     if (t >= a.T) return;
@@ -813,50 +851,62 @@ __global__ __launch_bounds__(256) void k_ring_out(EnhanceArgs a) {
     for (int x = threadIdx.x; x < a.H; x += 256) dst[x] = Elem<TIn>::load(A + x);
 }
 
-// per-slot reciprocal norms: one workgroup per (pool layer, slot); the workgroups past
-// them write the band/field operands of k_cols (the same for every layer and
-// tile), entry (e, hi/lo) for e = {0, 1, 3, 5}[tg] + s, and α of each layer
-__device__ __forceinline__ void slot_norm_block(const EnhanceArgs &a, int bid) {
-    __shared__ float red[4];
-    const int nsn = a.n_pool_layers * kSlots;
-    if (bid >= nsn + kTabEntries / 256) {  // α of each layer of the call
-        const int l = (bid - nsn - kTabEntries / 256) * 256 + threadIdx.x;
+// the band/field operands of k_cols (the same for every layer and tile),
+// entry (e, hi/lo) for e = {0, 1, 3, 5}[tg] + s (the first kTabEntries/256
+// workgroups), then α of each layer of the call
+__device__ void call_tables_block(const EnhanceArgs &a, int bid) {
+    if (bid >= kTabEntries / 256) {
+        const int l = (bid - kTabEntries / 256) * 256 + threadIdx.x;
         if (l < a.L) a.alpha_tab[l] = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
         return;
     }
-    if (bid >= nsn) {
-        const int idx = (bid - nsn) * 256 + threadIdx.x;
-        const int ln = idx % 64;
-        const int ent = idx / 128, hl = (idx / 64) & 1;
-        const int tg = ent >= 5 ? 3 : ent >= 3 ? 2 : ent >= 1 ? 1 : 0;
-        const int st = ent - (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5);
-        float v[8];
+    const int idx = bid * 256 + threadIdx.x;
+    const int ln = idx % 64;
+    const int ent = idx / 128, hl = (idx / 64) & 1;
+    const int tg = ent >= 5 ? 3 : ent >= 3 ? 2 : ent >= 1 ? 1 : 0;
+    const int st = ent - (tg == 0 ? 0 : tg == 1 ? 1 : tg == 2 ? 3 : 5);
+    float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = band_field_coef(16 * tg + (ln & 15), 32 * st + 8 * (ln >> 4) + e, a.R, a.ema_gamma);
-        uint16_t hi[8], lo[8], pick[8];
-        split8(v, hi, lo);
+    for (int e = 0; e < 8; ++e)
+        v[e] = band_field_coef(16 * tg + (ln & 15), 32 * st + 8 * (ln >> 4) + e, a.R, a.ema_gamma);
+    uint16_t hi[8], lo[8], pick[8];
+    split8(v, hi, lo);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pick[e] = hl ? lo[e] : hi[e];
-        put8(a.coef + (long)idx * 8, pick);
-        return;
-    }
-    const int pl = bid / kSlots, slot = bid % kSlots;
-    float ss = 0.f;
-    if (slot < a.n_slots) {
-        const float *P = a.pool + (long)pl * a.pool_stride + (long)slot * a.H;
-        for (int x = threadIdx.x; x < a.H; x += 256) ss = fmaf(P[x], P[x], ss);
-    }
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        a.slot_norm[pl * kSlots + slot] = 1.f / fmaxf(sqrtf(red[0] + red[1] + red[2] + red[3]), 1e-12f);
+    for (int e = 0; e < 8; ++e) pick[e] = hl ? lo[e] : hi[e];
+    put8(a.coef + (long)idx * 8, pick);
 }
 
-// k_prep: the pool operands (the first n_pool_layers·H/32 workgroups) and the
-// slot norms, operand table and α (the rest), in one launch
-__global__ __launch_bounds__(256) void k_prep(EnhanceArgs a) {
+// 1/|s| and max_x |s[x]| of one slot: one workgroup per (pool layer, slot)
+__device__ __forceinline__ void slot_norm_block(const EnhanceArgs &a, int bid) {
+    __shared__ float red[4], redm[4];
+    const int pl = bid / kSlots, slot = bid % kSlots;
+    float ss = 0.f, mx = 0.f;
+    if (slot < a.n_slots) {
+        const float *P = a.pool + (long)pl * a.pool_stride + (long)slot * a.H;
+        for (int x = threadIdx.x; x < a.H; x += 256) {
+            ss = fmaf(P[x], P[x], ss);
+            mx = fmaxf(mx, fabsf(P[x]));
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        ss += __shfl_xor(ss, o);
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6] = ss;
+        redm[threadIdx.x >> 6] = mx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float *hdr = reinterpret_cast<float *>(pool_rec(a, pl));
+        hdr[slot] = 1.f / fmaxf(sqrtf(red[0] + red[1] + red[2] + red[3]), 1e-12f);
+        hdr[kSlots + slot] = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+    }
+}
+
+// k_pool_prep: the operand tables (the first n_pool_layers·H/32 workgroups),
+// then the slot norms, of every pool layer
+__global__ __launch_bounds__(256) void k_pool_prep(EnhanceArgs a) {
     const int npp = a.n_pool_layers * (a.H / 32);
     if ((int)blockIdx.x < npp) pool_prep_block(a, blockIdx.x);
     else slot_norm_block(a, blockIdx.x - npp);
@@ -864,20 +914,18 @@ __global__ __launch_bounds__(256) void k_prep(EnhanceArgs a) {
 
 template <typename TIn, typename TOut>
 hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(k_prep,
-                       dim3(a.n_pool_layers * (a.H / 32) + a.n_pool_layers * kSlots + kTabEntries / 256 +
-                            (a.L + 255) / 256),
-                       dim3(256), 0, stream, a);
+    if (a.prepare_pool)
+        hipLaunchKernelGGL(k_pool_prep, dim3(a.n_pool_layers * (a.H / 32 + kSlots)), dim3(256), 0, stream, a);
     if (a.H > kAggMaxH) {  // k_sem computes the tile aggregates itself up to kAggMaxH
         const int fchunks = a.H / (16 / (int)sizeof(TIn));
         hipLaunchKernelGGL((k_field_agg<TIn>), dim3(a.L * a.ntiles * ((fchunks + 255) / 256)), dim3(256), 0,
                            stream, a);
     }
-    hipLaunchKernelGGL((k_sem<TIn>), dim3(a.L * a.ntiles), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_field_carry, dim3(a.L * (a.H / kFcCols)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_sem<TIn>), dim3(a.L * a.ntiles + a.L * a.R), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_field_carry<TIn>), dim3(a.L * (a.H / kFcCols) + kCallTableBlocks(a) + a.L * a.R),
+                       dim3(256), 0, stream, a);
     hipLaunchKernelGGL((k_cols<TIn, TOut>), dim3(a.L * a.ntiles * ((a.H + kCB - 1) / kCB)), dim3(256), 0,
                        stream, a);
-    hipLaunchKernelGGL((k_ring_out<TIn>), dim3(a.L * a.R), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -885,15 +933,21 @@ hipError_t launch_t(const EnhanceArgs &a, hipStream_t stream) {
 
 size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers) {
     const size_t nt = ((size_t)T + kTile - 1) / kTile;
-    const size_t floats = 2 * (size_t)L * nt * H + (size_t)n_pool_layers * kSlots;
-    // poolA and poolT: H/32 steps x 4 tiles (resp. H/16 x 2 steps) x hi/lo x 512 bf16
-    const size_t ops = (size_t)n_pool_layers * (size_t)H * 64 * 2 * 2;
+    // prepared pool records (a multiple of 256 bytes each)
+    const size_t recs = (size_t)n_pool_layers * (size_t)pool_rec_bytes(H);
+    // field aggregates and carries, and the carried ring [L][R <= 16][H]
+    const size_t floats = 2 * (size_t)L * nt * H + (size_t)L * kMaxWindow * H;
     // semantic weights: per tile 4 token groups x 2 k-steps x hi/lo x 512 bf16;
-    // the band/field and identity operand table
+    // the band/field operand table
     const size_t wsem = (size_t)L * nt * 4 * 4 * kOpElems + (size_t)kTabEntries * 8;
     // α per layer, rounded up to 64 floats
     const size_t alphas = ((size_t)L + 63) / 64 * 64;
-    return (floats + alphas) * sizeof(float) + (ops + wsem) * sizeof(uint16_t);
+    return recs + (floats + alphas) * sizeof(float) + wsem * sizeof(uint16_t);
+}
+
+hipError_t launch_pool_prepare(const EnhanceArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL(k_pool_prep, dim3(a.n_pool_layers * (a.H / 32 + kSlots)), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream) {

@@ -277,53 +277,138 @@ size_t sfa_enhance_workspace_size(int L, int T, int H) {
     return sfa::enhance_workspace_bytes(L, T, H, L);
 }
 
-int sfa_enhance(const void *attn, void *out, float *ring, float *field, const float *pool,
-                long long pool_layer_stride, float *enhancement, int L, int layer0, int n_layers,
-                int T, int H, int t0, float alpha_base, float cross_decay, float ema_gamma,
-                float temperature, float clip, int ring_size, int n_slots, int in_dtype,
-                int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+size_t sfa_enhance_pool_bytes(int n_pool_layers, int H) {
+    if (n_pool_layers <= 0 || H <= 0) return 0;
+    return (size_t)n_pool_layers * (size_t)sfa::pool_rec_bytes(H);
+}
+
+namespace {
+
+// checks shared by the enhancement entry points (pool and workspace aside):
+// SFA_OK, an error code, or kNothingToDo for zero-sized work
+int enhance_check(const void *attn, void *out, float *ring, float *field, float *enhancement, int L,
+                  int layer0, int n_layers, int T, int H, int t0, float temperature, float clip,
+                  int ring_size, int n_slots, int in_dtype, int out_dtype) {
     if (L < 0 || T < 0 || H <= 0 || layer0 < 0 || t0 < 0 || n_layers < layer0 + L || n_layers < 1)
         return SFA_ERR_INVALID_ARG;
     if (ring_size < 1 || ring_size > SFA_MAX_WINDOW || n_slots < 1 || n_slots > 64)
         return SFA_ERR_INVALID_ARG;
-    if (!(temperature > 0.f) || !(clip >= 0.f) || pool_layer_stride < 0) return SFA_ERR_INVALID_ARG;
+    if (!(temperature > 0.f) || !(clip >= 0.f)) return SFA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return SFA_ERR_UNSUPPORTED;
     if (H % 64 != 0) return SFA_ERR_UNSUPPORTED;
     // token indices of the last tile and the workgroup numbers are 32-bit
     if (T > INT_MAX - sfa::kTile) return SFA_ERR_INVALID_ARG;
     if ((long long)L * ((T + sfa::kTile - 1) / sfa::kTile) * ((H + 127) / 128) >= (1LL << 31))
         return SFA_ERR_INVALID_ARG;
-    if (L == 0 || T == 0) return SFA_OK;
-    if (!attn || !out || !ring || !field || !pool || !workspace) return SFA_ERR_INVALID_ARG;
-    if (pool_layer_stride != 0 && pool_layer_stride < (long long)n_slots * H) return SFA_ERR_INVALID_ARG;
+    if (L == 0 || T == 0) return kNothingToDo;
+    if (!attn || !out || !ring || !field) return SFA_ERR_INVALID_ARG;
     if (!aligned(attn, 16) || !aligned(out, 16) || !aligned(ring, 16) || !aligned(field, 16) ||
-        !aligned(pool, 16) || (enhancement && !aligned(enhancement, 16)) || !aligned(workspace, 16) ||
-        (pool_layer_stride % 4) != 0)
+        (enhancement && !aligned(enhancement, 16)))
         return SFA_ERR_INVALID_ARG;
-    const int n_pool_layers = pool_layer_stride == 0 ? 1 : L;
-    if (workspace_bytes < sfa::enhance_workspace_bytes(L, T, H, n_pool_layers)) return SFA_ERR_INVALID_ARG;
+    return SFA_OK;
+}
 
-    sfa::EnhanceArgs a;
-    a.attn = attn; a.out = out; a.ring = ring; a.field = field;
-    a.pool = pool; a.pool_stride = pool_layer_stride; a.enhancement = enhancement;
+sfa::EnhanceArgs enhance_args(const void *attn, void *out, float *ring, float *field, float *enhancement,
+                              int L, int layer0, int n_layers, int T, int H, int t0, float alpha_base,
+                              float cross_decay, float ema_gamma, float temperature, float clip,
+                              int ring_size, int n_slots, int in_dtype, int out_dtype) {
+    sfa::EnhanceArgs a{};
+    a.attn = attn; a.out = out; a.ring = ring; a.field = field; a.enhancement = enhancement;
     a.L = L; a.layer0 = layer0; a.n_layers = n_layers; a.T = T; a.H = H; a.t0 = t0;
-    a.R = ring_size; a.n_slots = n_slots; a.n_pool_layers = n_pool_layers;
+    a.R = ring_size; a.n_slots = n_slots;
     a.ntiles = (T + sfa::kTile - 1) / sfa::kTile;
     a.alpha_base = alpha_base; a.cross_decay = cross_decay; a.ema_gamma = ema_gamma;
     a.inv_temp_log2e = 1.4426950408889634f / temperature;
     a.clip = clip;
     a.in_bf16 = in_dtype == SFA_BF16;
     a.out_bf16 = out_dtype == SFA_BF16;
-    const size_t per = (size_t)L * a.ntiles * H;
-    float *ws = static_cast<float *>(workspace);
+    return a;
+}
+
+// the workspace after the pool records: field aggregates and carries, the
+// carried ring, the slot weights, the operand table and α per layer
+void carve_enhance_workspace(sfa::EnhanceArgs &a, unsigned char *rest) {
+    const size_t per = (size_t)a.L * a.ntiles * a.H;
+    float *ws = reinterpret_cast<float *>(rest);
     a.agg64 = ws;
     a.carry = ws + per;
-    a.slot_norm = ws + 2 * per;
-    a.poolA = reinterpret_cast<uint16_t *>(ws + 2 * per + (size_t)n_pool_layers * 64);
-    a.poolT = a.poolA + (size_t)n_pool_layers * H * 128;
-    a.wsem = a.poolT + (size_t)n_pool_layers * H * 128;
-    a.coef = a.wsem + (size_t)L * a.ntiles * 4 * 4 * 512;
+    a.halo = ws + 2 * per;
+    a.wsem = reinterpret_cast<uint16_t *>(ws + 2 * per + (size_t)a.L * SFA_MAX_WINDOW * a.H);
+    a.coef = a.wsem + (size_t)a.L * a.ntiles * 4 * 4 * 512;
     a.alpha_tab = reinterpret_cast<float *>(a.coef + (size_t)8 * 2 * 64 * 8);
+}
+
+}  // namespace
+
+int sfa_enhance(const void *attn, void *out, float *ring, float *field, const float *pool,
+                long long pool_layer_stride, float *enhancement, int L, int layer0, int n_layers,
+                int T, int H, int t0, float alpha_base, float cross_decay, float ema_gamma,
+                float temperature, float clip, int ring_size, int n_slots, int in_dtype,
+                int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (pool_layer_stride < 0) return SFA_ERR_INVALID_ARG;
+    const int chk = enhance_check(attn, out, ring, field, enhancement, L, layer0, n_layers, T, H, t0,
+                                  temperature, clip, ring_size, n_slots, in_dtype, out_dtype);
+    if (chk == kNothingToDo) return SFA_OK;
+    if (chk != SFA_OK) return chk;
+    if (!pool || !workspace) return SFA_ERR_INVALID_ARG;
+    if (pool_layer_stride != 0 && pool_layer_stride < (long long)n_slots * H) return SFA_ERR_INVALID_ARG;
+    if (!aligned(pool, 16) || !aligned(workspace, 16) || (pool_layer_stride % 4) != 0)
+        return SFA_ERR_INVALID_ARG;
+    const int n_pool_layers = pool_layer_stride == 0 ? 1 : L;
+    if (workspace_bytes < sfa::enhance_workspace_bytes(L, T, H, n_pool_layers)) return SFA_ERR_INVALID_ARG;
+
+    sfa::EnhanceArgs a = enhance_args(attn, out, ring, field, enhancement, L, layer0, n_layers, T, H, t0,
+                                      alpha_base, cross_decay, ema_gamma, temperature, clip, ring_size,
+                                      n_slots, in_dtype, out_dtype);
+    a.pool = pool; a.pool_stride = pool_layer_stride; a.n_pool_layers = n_pool_layers;
+    a.pool_rec = static_cast<unsigned char *>(workspace);
+    a.pool_rec_bytes = sfa::pool_rec_bytes(H);
+    a.prepare_pool = 1;
+    carve_enhance_workspace(a, a.pool_rec + (size_t)n_pool_layers * a.pool_rec_bytes);
+    return hip_status(sfa::launch_enhance(a, static_cast<hipStream_t>(stream)));
+}
+
+int sfa_enhance_prepare_pool(const float *pool, long long pool_layer_stride, int n_pool_layers,
+                             int n_slots, int H, void *prepared, size_t prepared_bytes, void *stream) {
+    if (n_pool_layers < 0 || n_slots < 1 || n_slots > 64 || H <= 0 || pool_layer_stride < 0)
+        return SFA_ERR_INVALID_ARG;
+    if (H % 64 != 0) return SFA_ERR_UNSUPPORTED;
+    if ((long long)n_pool_layers * (H / 32 + 64) >= (1LL << 31)) return SFA_ERR_INVALID_ARG;
+    if (n_pool_layers == 0) return SFA_OK;
+    if (!pool || !prepared) return SFA_ERR_INVALID_ARG;
+    if (n_pool_layers > 1 && pool_layer_stride < (long long)n_slots * H) return SFA_ERR_INVALID_ARG;
+    if (!aligned(pool, 16) || !aligned(prepared, 256) || (pool_layer_stride % 4) != 0)
+        return SFA_ERR_INVALID_ARG;
+    if (prepared_bytes < sfa_enhance_pool_bytes(n_pool_layers, H)) return SFA_ERR_INVALID_ARG;
+    sfa::EnhanceArgs a{};
+    a.pool = pool; a.pool_stride = pool_layer_stride; a.n_pool_layers = n_pool_layers;
+    a.n_slots = n_slots; a.H = H;
+    a.pool_rec = static_cast<unsigned char *>(prepared);
+    a.pool_rec_bytes = sfa::pool_rec_bytes(H);
+    return hip_status(sfa::launch_pool_prepare(a, static_cast<hipStream_t>(stream)));
+}
+
+int sfa_enhance_prepared(const void *attn, void *out, float *ring, float *field, const void *prepared,
+                         int shared_pool, float *enhancement, int L, int layer0, int n_layers, int T,
+                         int H, int t0, float alpha_base, float cross_decay, float ema_gamma,
+                         float temperature, float clip, int ring_size, int n_slots, int in_dtype,
+                         int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    const int chk = enhance_check(attn, out, ring, field, enhancement, L, layer0, n_layers, T, H, t0,
+                                  temperature, clip, ring_size, n_slots, in_dtype, out_dtype);
+    if (chk == kNothingToDo) return SFA_OK;
+    if (chk != SFA_OK) return chk;
+    if (!prepared || !workspace || !aligned(prepared, 256) || !aligned(workspace, 16))
+        return SFA_ERR_INVALID_ARG;
+    if (workspace_bytes < sfa::enhance_workspace_bytes(L, T, H, 0)) return SFA_ERR_INVALID_ARG;
+    sfa::EnhanceArgs a = enhance_args(attn, out, ring, field, enhancement, L, layer0, n_layers, T, H, t0,
+                                      alpha_base, cross_decay, ema_gamma, temperature, clip, ring_size,
+                                      n_slots, in_dtype, out_dtype);
+    a.pool = nullptr; a.pool_stride = 0;
+    a.n_pool_layers = shared_pool ? 1 : L;
+    a.pool_rec = static_cast<unsigned char *>(const_cast<void *>(prepared));
+    a.pool_rec_bytes = sfa::pool_rec_bytes(H);
+    a.prepare_pool = 0;
+    carve_enhance_workspace(a, static_cast<unsigned char *>(workspace));
     return hip_status(sfa::launch_enhance(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -35,8 +35,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     __bf16 b = (__bf16)x;
     return __builtin_bit_cast(uint16_t, b);
 }
+// two values rounded to bf16 in one dword (lo in bits 0..15); one packed
+// conversion (v_cvt_pk_bf16_f32 with both sources), the same rounding as two
+// single conversions
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // ---- cross-lane reductions over the four 16-lane groups (l ^ 16, l ^ 32) ----

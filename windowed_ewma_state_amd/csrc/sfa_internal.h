@@ -71,18 +71,30 @@ struct EnhanceArgs {
     int L, layer0, n_layers, T, H, t0, R, n_slots, ntiles, n_pool_layers;
     float alpha_base, cross_decay, ema_gamma, inv_temp_log2e, clip;
     int in_bf16, out_bf16;
+    // prepared pool: one record of pool_rec_bytes per pool layer (in the
+    // workspace when the call prepares it, else the caller's buffer):
+    //   floats [0, 64)     1 / |slot|
+    //   floats [64, 128)   max_x |slot[x]| of each slot
+    //   bytes  [1024, ..)  poolA [H/32][4][2][64][8] bf16 hi/lo, cosine operand,
+    //                      then poolT [H/16][2][2][64][8] bf16 hi/lo, semantic operand
+    unsigned char *pool_rec;
+    long long pool_rec_bytes;
+    int prepare_pool;       // the call prepares the records (sfa_enhance) or finds them ready
     // workspace carve-up
     float *agg64;           // [L][ntiles][H]   EMA of each 64-token tile from zero
     float *carry;           // [L][ntiles][H]   field just before each tile
-    float *slot_norm;       // [n_pool_layers][64]  1 / |slot|
-    uint16_t *poolA;        // [n_pool_layers][H/32][4][2][64][8] bf16 hi/lo, cosine operand
-    uint16_t *poolT;        // [n_pool_layers][H/16][2][2][64][8] bf16 hi/lo, semantic operand
+    float *halo;            // [L][R][H]        the carried ring, read before the ring is rewritten
     uint16_t *wsem;         // [L][ntiles][4][2][2][64][8] bf16 hi/lo of 0.5·(slot weights)
     uint16_t *coef;         // [8 x 2][64][8] band/field operands
     float *alpha_tab;       // [L] α of each layer of the call
 };
+constexpr int kPoolRecHeader = 1024;  // bytes before the operands in a pool record
+__host__ __device__ constexpr long long pool_rec_bytes(int H) { return kPoolRecHeader + 512LL * H; }
+// workspace bytes of a call: with n_pool_layers > 0 the call also prepares that
+// many pool records in the workspace
 size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers);
 hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream);
+hipError_t launch_pool_prepare(const EnhanceArgs &a, hipStream_t stream);
 
 // XCD-aware block remap: consecutive logical indices land on the same XCD
 // (hardware dispatches workgroups round-robin over the 8 XCDs of an MI355X).

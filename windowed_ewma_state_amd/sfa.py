@@ -259,3 +259,80 @@ def enhance(attn, pool, ring, field, *, layer0: int = 0, n_layers: int | None = 
         _stream(stream, dev))
     _lib.check(st, "sfa_enhance")
     return out, enhancement
+
+
+class PreparedPool:
+    """The MFMA-operand form of a read-only semantic pool (sfa_enhance_prepare_pool):
+    `buf` is a uint8 device tensor of sfa_enhance_pool_bytes(n_layers, H) bytes."""
+
+    def __init__(self, buf, n_layers: int, n_slots: int, H: int, shared: bool):
+        self.buf, self.n_layers, self.n_slots, self.H, self.shared = buf, n_layers, n_slots, H, shared
+
+    def layer_offset(self, layer0: int) -> "PreparedPool":
+        """The records from pool layer `layer0` on (a call that starts at that global layer)."""
+        if self.shared:
+            return self
+        rec = int(_lib.lib().sfa_enhance_pool_bytes(1, self.H))
+        return PreparedPool(self.buf[layer0 * rec:], self.n_layers - layer0, self.n_slots, self.H, False)
+
+
+def enhance_pool_bytes(n_pool_layers: int, H: int) -> int:
+    return int(_lib.lib().sfa_enhance_pool_bytes(n_pool_layers, H))
+
+
+@_on_call_stream
+def enhance_prepare_pool(pool, *, shared_pool: bool = False, stream=None) -> PreparedPool:
+    """sfa_enhance_prepare_pool: pool [L,n_slots,H] fp32 (or [n_slots,H] with
+    shared_pool=True) -> its prepared form, kept by the caller for later calls
+    of enhance_prepared."""
+    dev = pool.device
+    if shared_pool:
+        n_layers, (n_slots, H) = 1, pool.shape
+        stride = 0
+    else:
+        n_layers, n_slots, H = pool.shape
+        stride = n_slots * H
+    nbytes = enhance_pool_bytes(n_layers, H)
+    buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = _lib.lib().sfa_enhance_prepare_pool(
+        _dev(pool, "pool", torch.float32, tuple(pool.shape), dev), stride, n_layers, n_slots, H,
+        _dev(buf, "prepared"), buf.numel(), _stream(stream, dev))
+    _lib.check(st, "sfa_enhance_prepare_pool")
+    return PreparedPool(buf, n_layers, n_slots, H, shared_pool)
+
+
+@_on_call_stream
+def enhance_prepared(attn, prepared: PreparedPool, ring, field, *, layer0: int = 0,
+                     n_layers: int | None = None, t0: int = 0, alpha_base: float = 0.1,
+                     cross_decay: float = 0.8, ema_gamma: float = 0.98, temperature: float = 0.07,
+                     clip: float = 0.5, out=None, out_dtype=None, enhancement=None, workspace=None,
+                     stream=None):
+    """sfa_enhance_prepared: enhance() with the pool in prepared form.  Layer i of
+    the call uses record i of `prepared` (record 0 for a shared pool): pass
+    prepared.layer_offset(layer0) for a call that starts at global layer layer0."""
+    L, T, H = attn.shape
+    R = ring.shape[1]
+    dev = attn.device
+    if prepared.H != H:
+        raise ValueError(f"pool prepared for hidden size {prepared.H}, attention has {H}")
+    if not prepared.shared and prepared.n_layers < L:
+        raise ValueError(f"{prepared.n_layers} prepared pool layers for a call over {L} layers")
+    in_code = _dtype_code(attn, "attn")
+    out_dtype = attn.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((L, T, H), dtype=out_dtype, device=dev)
+    out_code = _dtype_code(out, "out")
+    nl = layer0 + L if n_layers is None else n_layers
+    if workspace is None:
+        workspace = torch.empty(max(enhance_workspace_size(L, T, H), 1), dtype=torch.uint8, device=dev)
+    st = _lib.lib().sfa_enhance_prepared(
+        _dev(attn, "attn", None, (L, T, H), dev), _dev(out, "out", None, (L, T, H), dev),
+        _dev(ring, "ring", torch.float32, (L, R, H), dev), _dev(field, "field", torch.float32, (L, H), dev),
+        _dev(prepared.buf, "prepared"), int(prepared.shared),
+        _dev(enhancement, "enhancement", torch.float32, (L, T, H), dev),
+        L, layer0, nl, T, H, t0, float(alpha_base), float(cross_decay), float(ema_gamma),
+        float(temperature), float(clip), R, prepared.n_slots, in_code, out_code,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream, dev))
+    _lib.check(st, "sfa_enhance_prepared")
+    return out, enhancement

@@ -141,12 +141,12 @@ def c2_attn_bytes():
 
 
 def run_c2(reps=40, sets=6):
-    """The 0.5B-shaped prefill call (scan + attention) on `sets` rotating input
-    sets of 67 MB each, more than the 256 MB MALL holds, so every call streams
-    from HBM.  A call's GPU time (~30 us) is about what the Python binding
-    takes to issue it, so the calls are captured once in HIP graphs and
-    replayed: `sets` whole calls per replay, and separately `sets` attention
-    parts (after one scan of each set into its own workspace).  HIP events on
+    """The 0.5B-shaped prefill call on `sets` rotating input sets of 67 MB
+    each, more than the 256 MB MALL holds, so every call streams from HBM.  A
+    call's GPU time (~20-30 us) is about what the Python binding takes to issue
+    it, so the calls are captured once in HIP graphs and replayed: `sets` whole
+    calls per replay (the single pass), the same as separate scan and attention
+    parts (the two-pass form), and the attention parts alone.  HIP events on
     the replay stream bracket `reps` back-to-back replays."""
     dev = torch.device("cuda:0")
     B_, N_, HQ_, HKV_, HD_ = C2["B"], C2["N"], C2["HQ"], C2["HKV"], C2["HD"]
@@ -179,7 +179,8 @@ def run_c2(reps=40, sets=6):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for d in bufs:
-                call(d, part)
+                for p in (part if isinstance(part, tuple) else (part,)):
+                    call(d, p)
         return g
 
     def per_call_ms(g):
@@ -195,8 +196,11 @@ def run_c2(reps=40, sets=6):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * sets)
 
+    # sfa_prefill (scan launches, then attention), its attention part alone,
+    # and the single pass (the scan folded into the attention kernel)
     ms = per_call_ms(graph_of(both))
     ms_attn = per_call_ms(graph_of(_lib.SFA_PREFILL_ATTEND))
+    ms_one = per_call_ms(graph_of(_lib.SFA_PREFILL_SINGLE_PASS))
     byts, abyts = c2_bytes(), c2_attn_bytes()
     return {"workload": "Qwen2.5-0.5B-shaped prefill, batch 4 x 4096 tokens, 14/2 heads, d 64, bf16 in/out, "
                         f"{sets} rotating input sets, HIP-graph replays",
@@ -205,7 +209,9 @@ def run_c2(reps=40, sets=6):
                          "unit": "GB/s", "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_call": byts},
             "attention": {"kernel": "k_window_attn (d 64)", "avg_launch_us": ms_attn * 1e3,
                           "achieved": abyts / (ms_attn * 1e-3) / 1e9, "frac": abyts / (ms_attn * 1e-3) / PEAK_HBM,
-                          "bytes_per_launch": abyts}}
+                          "bytes_per_launch": abyts},
+            "single_pass": {"us_per_call": ms_one * 1e3, "frac": byts / (ms_one * 1e-3) / PEAK_HBM,
+                            "launches": "k_fused_init, k_window_attn with the scan folded in"}}
 
 
 # ----------------------------------------------------------------------------

@@ -140,10 +140,23 @@ int sfa_prefill(const void *q, const void *k, const void *v,
  *                       (reads the carries from the workspace), and the ring
  *                       hand-off.  Must run after SCAN with the same arguments
  *                       and workspace, on the same stream (or ordered after it).
- * parts = SCAN | ATTEND is exactly sfa_prefill.  Other values of `parts`
- * return SFA_ERR_INVALID_ARG.
+ * parts = SCAN | ATTEND is exactly sfa_prefill.
+ *   SFA_PREFILL_SINGLE_PASS  the whole call in one pass over the inputs (no
+ *                       scan launches, K read once): every attention
+ *                       workgroup forms its 64-token chunk's EWMA aggregate
+ *                       from its own keys, publishes it in the workspace, and
+ *                       folds those of the chunks before it onto the carried S
+ *                       (first page, section 2.1 far-field equation, as a
+ *                       chunked scan).  Same results and arguments as
+ *                       sfa_prefill, for bf16 inputs and at most 64 chunks
+ *                       (4096 tokens) per sequence; other calls return
+ *                       SFA_ERR_UNSUPPORTED.  It is measured slower than
+ *                       sfa_prefill (the waits for the published aggregates
+ *                       cost more than the separate scan) and offered for
+ *                       callers that must not read K twice.
+ * Other values of `parts` return SFA_ERR_INVALID_ARG.
  */
-enum { SFA_PREFILL_SCAN = 1, SFA_PREFILL_ATTEND = 2 };
+enum { SFA_PREFILL_SCAN = 1, SFA_PREFILL_ATTEND = 2, SFA_PREFILL_SINGLE_PASS = 4 };
 int sfa_prefill_part(int parts, const void *q, const void *k, const void *v,
                      const float *gamma, const float *alpha,
                      void *out, void *ring_k, void *ring_v, float *state,

@@ -96,6 +96,21 @@ def test_prefill_rejects_before_launch(kw, want):
 
 
 @pytest.mark.parametrize("kw,want", [
+    (dict(parts=3), OK), (dict(parts=0), INV), (dict(parts=5), INV), (dict(parts=8), INV),
+    (dict(parts=4, in_dtype=0), UNS), (dict(parts=4, n=64 * 64 + 1), UNS),
+    (dict(parts=4, n=64 * 64, q=None), INV), (dict(parts=4, B=0, q=None), OK),
+])
+def test_prefill_part_modes(kw, want):
+    args = dict(parts=3, q=P, k=P, v=P, gamma=P, alpha=P, out=P, ring_k=P, ring_v=P, state=P, pos0=None,
+                B=1, n=8, Hq=2, Hkv=1, d=64, window=16, scale=0.0, in_dtype=1, out_dtype=0,
+                ws=P, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    if want == OK and args["B"] != 0:
+        return  # a valid call would launch: not on the host
+    assert _lib.lib().sfa_prefill_part(*args.values()) == want
+
+
+@pytest.mark.parametrize("kw,want", [
     (dict(window=0), INV), (dict(Hq=5, Hkv=2), INV), (dict(d=32), UNS), (dict(in_dtype=3), UNS),
     (dict(pos=None), INV), (dict(state=None), INV), (dict(ring_k=P + 8), INV),
     (dict(L=0, q=None), OK), (dict(B=0, pos=None), OK),

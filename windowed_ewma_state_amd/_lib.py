@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libsfa.so")
 SFA_OK, SFA_ERR_INVALID_ARG, SFA_ERR_UNSUPPORTED, SFA_ERR_HIP, SFA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 SFA_NOALLOC_SCRATCH_BYTES = 16 << 20
 SFA_F32, SFA_BF16 = 0, 1
-SFA_PREFILL_SCAN, SFA_PREFILL_ATTEND = 1, 2
+SFA_PREFILL_SCAN, SFA_PREFILL_ATTEND, SFA_PREFILL_SINGLE_PASS = 1, 2, 4
 
 # every symbol include/sfa.h declares
 EXPORTS = ("sfa_status_string", "sfa_abi_version", "sfa_prefill_workspace_size", "sfa_prefill",

@@ -20,6 +20,16 @@
 //                 bf16 hi + lo) and the α·S epilogue.
 // A fourth, tiny launch copies the last W keys/values into the ring when the
 // call continues an existing cache (the first tile reads the old ring).
+//
+// Single pass (on request; S per KV head, bf16 inputs, at most 64 tiles per
+// sequence):
+//   k_fused_init  clears the published-aggregate words, saves the carried S;
+//   k_window_attn<.., FUSED> forms each tile's aggregate from its own scan,
+//                 publishes it, and folds those of the earlier tiles of its
+//                 sequence (no scan launches, K read once).
+// Measured slower than the two launches of the scan on every workload tried:
+// the workgroups wait for the published aggregates, whose round trips queue
+// behind the streaming Q/K/V/O traffic.
 #include <type_traits>
 
 #include "sfa_common.h"
@@ -167,7 +177,10 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
             if (p >= W) bw = gm * bw + (1.f - gm) / (float)(p - W + 1);
         }
     }
-    if (lane_ok) {
+    // (S per KV head with bf16 inputs, the attention kernel forms the block
+    // aggregates from its own scan and reads only the tile carries)
+    constexpr bool kWrite16 = RM || QH || sizeof(TIn) != 2;
+    if (lane_ok && kWrite16) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
@@ -375,6 +388,122 @@ __device__ __forceinline__ void row_scan_step(f32x4 (*V)[2], float &A, int c16) 
     A = c16 >= SH ? A * Ap : A;
 }
 
+// ---------------------------------------------------------------------------
+// Single pass (S per KV head, bf16 inputs, at most kFusedMaxTiles tiles per
+// sequence): no scan launches.  Each attention workgroup publishes its tile's
+// aggregate (the EWMA of the tile's evicted keys from zero) and folds the
+// aggregates of the earlier tiles of its sequence onto the carried S.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kAggTag = 1ull << 32;  // high word of a published aggregate element
+constexpr int kSpinLimit = 1 << 20;       // polls before a workgroup gives up waiting
+
+// workgroup -> (chain, tile) with the tiles of a chain in dispatch order, so a
+// workgroup only ever waits for workgroups dispatched before it.  With a
+// multiple of 8 chains, chain c runs on XCD c mod 8 (consecutive tiles share
+// that XCD's L2 for the K/V halo); otherwise in workgroup order.
+__device__ __forceinline__ int fused_tile_order(int bid, int nchains, int ntiles) {
+    if (nchains % 8 == 0) {
+        const int xcd = bid % 8, idx = bid / 8;
+        return ((idx / ntiles) * 8 + xcd) * ntiles + idx % ntiles;
+    }
+    return bid;
+}
+
+// S before tile `tile` of chain bg: wave 0 first publishes this tile's
+// aggregate (its four blocks composed, from the block aggregates in LDS); then
+// the earlier tiles are split into four contiguous ranges, wave w folds range
+// w as (Γ_w, X_w) = (decay over the range, EWMA of the range from zero), and
+// C = the carried S composed with the four ranges in order.
+template <int D, int EPL>
+__device__ __forceinline__ void fused_carry(const PrefillArgs &a, int bg, int tile, int p0, float gm, int wave,
+                                            int lane, int e0, const float (*BlkAgg)[D], float (*FoldX)[D],
+                                            float *FoldG, float *C) {
+    const int n = a.n, W = a.W;
+    uint64_t *rec = a.tagged + (long)bg * a.ntiles * D;
+    auto tile_decay = [&](int j) {
+        const int s0 = j * kTile;
+        return powi(gm, evict_steps(p0, s0, min(kTile, n - s0), W));
+    };
+    if (wave == 0) {
+        float X[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) X[e] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int s0 = tile * kTile + kBlk * w;
+            const float gl = s0 < n ? powi(gm, evict_steps(p0, s0, min(kBlk, n - s0), W)) : 1.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) X[e] = gl * X[e] + BlkAgg[w][e0 + e];
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            __hip_atomic_store(rec + (long)tile * D + e0 + e, kAggTag | __float_as_uint(X[e]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    constexpr int kPer = (kFusedMaxTiles + 3) / 4;  // earlier tiles per wave, at most
+    const int per = (tile + 3) / 4;
+    const int j0 = min(wave * per, tile), j1 = min(j0 + per, tile);
+    uint64_t v[kPer][EPL];
+    bool ready = false;
+    for (int it = 0; it < kSpinLimit && !ready; ++it) {
+        if (it > 0) __builtin_amdgcn_s_sleep(2);
+        bool ok = true;
+#pragma unroll
+        for (int jj = 0; jj < kPer; ++jj) {
+            if (j0 + jj < j1) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    v[jj][e] = __hip_atomic_load(rec + (long)(j0 + jj) * D + e0 + e, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                    ok = ok && (v[jj][e] >> 32) == (kAggTag >> 32);
+                }
+            }
+        }
+        ready = __builtin_amdgcn_ballot_w64(!ok) == 0;  // every lane's words published
+    }
+    float X[EPL], G = 1.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) X[e] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < kPer; ++jj) {
+        if (j0 + jj < j1) {
+            const float g = tile_decay(j0 + jj);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) X[e] = g * X[e] + __uint_as_float((uint32_t)v[jj][e]);
+            G *= g;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) FoldX[wave][e0 + e] = X[e];
+    if (lane == 0) FoldG[wave] = G;
+    __syncthreads();
+    const float *si = a.sinit + (long)bg * D + e0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) C[e] = si[e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) C[e] = FoldG[w] * C[e] + FoldX[w][e0 + e];
+}
+
+// before the single pass: clear the published-aggregate words (tag 0: not yet
+// published) and take the carried S (or 0) out of `state`, which the pass
+// itself overwrites with the final S
+__global__ __launch_bounds__(256) void k_fused_init(PrefillArgs a) {
+    const long words = (long)a.B * a.Hkv * a.ntiles * a.d;
+    const long zero_blocks = (words / 2 + 255) / 256;
+    if ((long)blockIdx.x < zero_blocks) {
+        const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 2;
+        if (i < words) *reinterpret_cast<u32x4 *>(a.tagged + i) = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
+    const long idx = ((long)blockIdx.x - zero_blocks) * 256 + threadIdx.x;
+    if (idx >= (long)a.B * a.Hkv * a.d) return;
+    const int b = (int)(idx / ((long)a.Hkv * a.d));
+    const bool carried = a.pos0 != nullptr && a.pos0[b] > 0;
+    a.sinit[idx] = carried ? a.state[idx] : 0.f;
+}
+
 template <typename TIn> struct Lds;
 template <> struct Lds<__bf16> { static constexpr int kpad = 8, vpad = 0; };
 template <> struct Lds<float> { static constexpr int kpad = 4, vpad = 4; };
@@ -421,7 +550,7 @@ __device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float *v) {
 // RM: the running mean of the keys that have left the window is the EWMA
 // input; the wave starts from the tile's carried (S, C) and the block
 // aggregates of its earlier blocks, then scans C += k, S = γS + (1-γ)·C/m.
-template <typename TIn, typename TOut, int D, int MODE>
+template <typename TIn, typename TOut, int D, int MODE, bool FUSED = false>
 __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     constexpr bool QH = MODE == kQueryHead, RM = MODE == kRunningMean;
     constexpr bool kBf16 = std::is_same<TIn, __bf16>::value;
@@ -438,10 +567,16 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // scan over the wave's 16 tokens); the LDS slot then only carries S at the
     // block start.  The other modes keep each token's S row in LDS.
     constexpr bool kRegS = !QH && !RM && kBf16;
+    static_assert(!FUSED || kRegS, "the single-pass form exists for S per KV head with bf16 inputs");
     __shared__ __attribute__((aligned(16))) float Sb[4][kRegS ? D : kBlk * SS];
+    // kRegS: each wave's block aggregate (the EWMA of its 16 tokens from zero);
+    // single pass: the waves' partial folds of the earlier tiles' aggregates
+    __shared__ __attribute__((aligned(16))) float BlkAgg[kRegS ? 4 : 1][kRegS ? D : 1];
+    __shared__ __attribute__((aligned(16))) float FoldX[FUSED ? 4 : 1][FUSED ? D : 1];
+    __shared__ float FoldG[4];
 
     const int nblk = a.B * a.Hkv * a.ntiles;
-    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int lid = FUSED ? fused_tile_order(blockIdx.x, a.B * a.Hkv, a.ntiles) : xcd_remap(blockIdx.x, nblk);
     const int tile = lid % a.ntiles;
     const int bg = lid / a.ntiles;
     const int b = bg / a.Hkv, G = bg % a.Hkv;
@@ -512,8 +647,18 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     };
     // QH: chain of query head h of this group
     const long chain0 = QH ? (long)b * a.Hq + (long)G * group : (long)bg;
-    float Cin[EPL], Ain[3][EPL];
-    carry_loads(chain0, Cin, Ain);
+    float Cin[EPL], Ain[kRegS ? 1 : 3][EPL];
+    if constexpr (kRegS) {
+        // the block aggregates come from this tile's own scan (step 3); the
+        // single pass folds the earlier tiles' aggregates instead of a carry
+        if constexpr (!FUSED) {
+            const float *C = a.carry + (chain0 * a.ntiles + tile) * D + e0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) Cin[e] = C[e];
+        }
+    } else {
+        carry_loads(chain0, Cin, Ain);
+    }
     // RM: the key sum carried into the tile and the earlier blocks' key sums
     float Kin[RM ? EPL : 1], Kblk[RM ? 3 : 1][RM ? EPL : 1];
     if constexpr (RM) {
@@ -656,7 +801,41 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // QH: the keys evicted by this wave's 16 tokens, kept in registers (the K
     // staging area is reused in the head loop)
     float kev[QH ? kBlk : 1][EPL];
-    if constexpr (!QH) {
+    float Ac = 1.f;  // kRegS: decay from the block start to the lane's token
+    if constexpr (kRegS) {
+        __syncthreads();
+        // ---- (3) EWMA through the block from zero, then the block aggregate ----
+        // lane (q4, c16) needs S_t for its token t = tb + c16 at
+        // d = 32k + 8q4 + 4half + i.  Per token the step is S = A·S + V with
+        // (A, V) = (γ, (1-γ)·k_{t-W}) if t evicts, else (1, 0); a log-step
+        // scan over the 16 lanes of the row composes them.  Lane c16 = 15 then
+        // holds the whole block's map: its V is the block's aggregate.
+        const int t = tb + c16;
+        const bool ev = t < n && p0 + t >= W;
+        Ac = ev ? gm : 1.f;
+        const float w1 = ev ? 1.f - gm : 0.f;
+        // token t - W sits in staged row (t - W) - (t0 - 16)
+        const TIn *kr = &Klds[(kBlk * wave + c16 + kMaxWindow - W) * KS + 8 * q4];
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+            const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(kr + 32 * k);
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Sreg[k][half][i] = w1 * (float)kk[4 * half + i];
+        }
+        row_scan_step<1, D / 32>(Sreg, Ac, c16);
+        row_scan_step<2, D / 32>(Sreg, Ac, c16);
+        row_scan_step<4, D / 32>(Sreg, Ac, c16);
+        row_scan_step<8, D / 32>(Sreg, Ac, c16);
+        if (c16 == kBlk - 1) {
+#pragma unroll
+            for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    *reinterpret_cast<f32x4 *>(&BlkAgg[wave][32 * k + 8 * q4 + 4 * half]) = Sreg[k][half];
+        }
+    } else if constexpr (!QH) {
         float S[EPL], Ck[RM ? EPL : 1];
         if constexpr (RM) {
             // (S, C) at the block start: each earlier block w maps them to
@@ -690,44 +869,6 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
         __syncthreads();
 
         // ---- (3) EWMA through the block: S_t after token t's own eviction -----
-        if constexpr (kRegS) {
-            // lane (q4, c16) needs S_t for its token t = tb + c16 at
-            // d = 32k + 8q4 + 4half + i.  Per token the step is S = A·S + V with
-            // (A, V) = (γ, (1-γ)·k_{t-W}) if t evicts, else (1, 0); a log-step
-            // scan over the 16 lanes of the row composes them, then
-            // S_t = A_{..t}·S_start + V_{..t}.
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) Sw[e0 + e] = S[e];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int t = tb + c16;
-            const bool ev = t < n && p0 + t >= W;
-            float Ac = ev ? gm : 1.f;
-            const float w1 = ev ? 1.f - gm : 0.f;
-            // token t - W sits in staged row (t - W) - (t0 - 16)
-            const TIn *kr = &Klds[(kBlk * wave + c16 + kMaxWindow - W) * KS + 8 * q4];
-#pragma unroll
-            for (int k = 0; k < D / 32; ++k) {
-                const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(kr + 32 * k);
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Sreg[k][half][i] = w1 * (float)kk[4 * half + i];
-            }
-            row_scan_step<1, D / 32>(Sreg, Ac, c16);
-            row_scan_step<2, D / 32>(Sreg, Ac, c16);
-            row_scan_step<4, D / 32>(Sreg, Ac, c16);
-            row_scan_step<8, D / 32>(Sreg, Ac, c16);
-#pragma unroll
-            for (int k = 0; k < D / 32; ++k)
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&Sw[32 * k + 8 * q4 + 4 * half]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Sreg[k][half][i] = fmaf(Ac, s0[i], Sreg[k][half][i]);
-                }
-        } else {
 #pragma unroll
         for (int j = 0; j < kBlk; ++j) {
             const int t = tb + j;
@@ -751,7 +892,6 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) Sw[j * SS + e0 + e] = S[e];
         }
-        }
     } else {
         __syncthreads();
 #pragma unroll
@@ -759,6 +899,49 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
             load_epl<TIn, EPL>(&Klds[(kBlk * wave + j + kMaxWindow - W) * KS + e0], kev[j]);
     }
     __syncthreads();
+    if constexpr (kRegS) {
+        // ---- S before the tile, and at this wave's block start ----------------
+        float C[EPL];
+        if constexpr (FUSED) {
+            fused_carry<D, EPL>(a, bg, tile, p0, gm, wave, lane, e0, BlkAgg, FoldX, FoldG, C);
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) C[e] = Cin[e];
+        }
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            if (w < wave) {
+                const int s0 = t0 + kBlk * w;
+                const float gl = powi(gm, evict_steps(p0, s0, min(kBlk, n - s0), W));
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) C[e] = gl * C[e] + BlkAgg[w][e0 + e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) Sw[e0 + e] = C[e];
+        wave_lds_sync();
+        // S_t = A_{..t}·S_start + V_{..t}
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&Sw[32 * k + 8 * q4 + 4 * half]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Sreg[k][half][i] = fmaf(Ac, s0[i], Sreg[k][half][i]);
+            }
+        if constexpr (FUSED) {
+            // the single pass writes S after the last token: lanes c16 = 15 of
+            // the last wave (tokens past the end leave S unchanged)
+            if (tile == a.ntiles - 1 && wave == 3 && c16 == kBlk - 1 && a.state) {
+                float *st = a.state + (long)bg * D;
+#pragma unroll
+                for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+                        *reinterpret_cast<f32x4 *>(st + 32 * k + 8 * q4 + 4 * half) = Sreg[k][half];
+            }
+        }
+    }
     // QH: S tile of query head h (its carry in Cin/Ain) into Sw; the next
     // head's carry loads go out here
     auto head_S = [&](int h) {
@@ -1025,6 +1208,18 @@ __global__ __launch_bounds__(256) void k_ring_handoff(PrefillArgs a) {
 template <typename TIn, typename TOut, int D>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t stream, int parts) {
     const unsigned tiles = (unsigned)(a.B * a.Hkv * a.ntiles);
+    if constexpr (std::is_same<TIn, __bf16>::value) {
+        // single pass (requested explicitly; the caller checked the limits)
+        if (parts == kPrefillSinglePass) {
+            const long words = (long)tiles * D;
+            const long init_blocks = (words / 2 + 255) / 256 + ((long)a.B * a.Hkv * D + 255) / 256;
+            hipLaunchKernelGGL(k_fused_init, dim3((unsigned)init_blocks), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kKvHead, true>), dim3(tiles), dim3(256), 0, stream, a);
+            if (a.pos0 && a.ring_k)
+                hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     if (parts & kPrefillScan) {
         // one wave per (tile, b, KV head); per query head it feeds the group's chains
         const unsigned scan_tiles = (unsigned)(a.B * a.Hkv * a.ntiles);

@@ -92,7 +92,8 @@ int prefill_check(int parts, int mode, const void *q, const void *k, const void 
                   const float *gamma, const float *alpha, void *out, void *ring_k, void *ring_v,
                   float *state, const int32_t *pos0, int B, int n, int Hq, int Hkv, int d, int window,
                   int in_dtype, int out_dtype) {
-    if (parts < 1 || parts > (SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND)) return SFA_ERR_INVALID_ARG;
+    if (parts != SFA_PREFILL_SINGLE_PASS && (parts < 1 || parts > (SFA_PREFILL_SCAN | SFA_PREFILL_ATTEND)))
+        return SFA_ERR_INVALID_ARG;
     if (B < 0 || n < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return SFA_ERR_INVALID_ARG;
     if (window < 1 || window > SFA_MAX_WINDOW) return SFA_ERR_INVALID_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return SFA_ERR_UNSUPPORTED;
@@ -104,6 +105,9 @@ int prefill_check(int parts, int mode, const void *q, const void *k, const void 
         const long long chains = (long long)B * (mode == sfa::kQueryHead ? Hq : Hkv);
         if (chains * ((n + sfa::kTile - 1) / sfa::kTile) * 4 >= (1LL << 31)) return SFA_ERR_INVALID_ARG;
     }
+    if (parts == SFA_PREFILL_SINGLE_PASS &&
+        (mode != sfa::kKvHead || in_dtype != SFA_BF16 || (n + sfa::kTile - 1) / sfa::kTile > sfa::kFusedMaxTiles))
+        return SFA_ERR_UNSUPPORTED;
     if (B == 0 || n == 0) return kNothingToDo;
     if (!q || !k || !v || !gamma || !alpha || !out) return SFA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -152,6 +156,10 @@ int prefill_impl(int parts, int mode, const void *q, const void *k, const void *
     a.agg64 = ws + 4 * per;
     a.carry = ws + 5 * per;
     a.csum16 = a.csum64 = a.ccarry = a.beta64 = nullptr;
+    // the single pass (when it applies) uses the same memory for its
+    // published aggregates [B*Hkv][ntiles][d] (8 bytes each) and the carried S
+    a.tagged = reinterpret_cast<uint64_t *>(ws);
+    a.sinit = ws + 2 * per;
     if (running_mean) {
         a.csum16 = ws + 6 * per;
         a.csum64 = ws + 10 * per;

@@ -56,9 +56,15 @@ struct PrefillArgs {
     // coefficient of the incoming C in the tile's outgoing S
     float *csum16, *csum64, *ccarry;  // as agg16, agg64, carry
     float *beta64;                    // [B*Hs][ntiles]
+    // single-pass form (S per KV head, bf16 inputs, at most kFusedMaxTiles tiles
+    // per sequence): every attention workgroup publishes its tile's EWMA
+    // aggregate as tagged words and folds those of the tiles before it
+    uint64_t *tagged;  // [B*Hkv][ntiles][d]  (fp32 bits, tag in the high word)
+    float *sinit;      // [B*Hkv][d]          S carried into the call (0 for a fresh sequence)
 };
+constexpr int kFusedMaxTiles = 64;
 size_t prefill_workspace_bytes(int B, int n, int Hkv, int d);
-constexpr int kPrefillScan = 1, kPrefillAttend = 2;
+constexpr int kPrefillScan = 1, kPrefillAttend = 2, kPrefillSinglePass = 4;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream, int parts);
 
 struct EnhanceArgs {

@@ -92,8 +92,9 @@ def prefill(q, k, v, gamma, alpha, *, window: int = 16, scale: float = 0.0, out=
     Returns (out, ring_k, ring_v, state).  ring_k/ring_v [B,Hkv,W,d] and
     state [B,Hkv,d] fp32 are allocated when not given; pass them (and pos0 [B]
     int32) to continue an existing cache.  `parts` (SFA_PREFILL_SCAN = 1,
-    SFA_PREFILL_ATTEND = 2) selects sfa_prefill_part; the two parts must share
-    every argument, including the workspace.  gamma_per_query_head=True calls
+    SFA_PREFILL_ATTEND = 2, or SFA_PREFILL_SINGLE_PASS = 4) selects
+    sfa_prefill_part; the two parts must share every argument, including the
+    workspace.  gamma_per_query_head=True calls
     sfa_prefill_qh: gamma [Hq] and state [B,Hq,d].  running_mean=True calls
     sfa_prefill_rm: state [B,Hkv,2,d] (S, then the mean of the keys that have
     left the window).

@@ -427,6 +427,83 @@ def run_variants(steps=10, warmup=2):
     return res
 
 
+def run_decode_enhance(reps=50, sets=4):
+    """The decode step fused with the triple-channel enhancement
+    (sfa_decode_step_enhance) on the 7B shape (28 layers, 28/4 heads, d 128,
+    hidden 3584, a 64-slot pool per layer, bf16 out): one sequence (the
+    engine's shape: every layer of one token), against the same work unfused
+    (sfa_decode_step, then sfa_enhance_prepared on its one-token rows), both
+    replayed from HIP graphs over `sets` rotating input sets; and a batch of 256
+    sequences through the fused form (each workgroup reads its layer's pool)."""
+    dev = torch.device("cuda:0")
+    L, Hq, Hkv, hd, R = 28, 28, 4, 128, 16
+    H = Hq * hd
+
+    def make(Bs, seed):
+        d = inputs.decode_inputs(L, Bs, Hq, Hkv, hd, seed=seed, device=dev)
+        pool = inputs.normal((L, 64, H), seed * 16 + 14, 1.0, torch.float32, dev)
+        d["prep"] = sfa.enhance_prepare_pool((pool / pool.norm(dim=-1, keepdim=True)).contiguous())
+        d["e_ring"] = torch.zeros((L, Bs, R, H), device=dev)
+        d["field"] = torch.zeros((L, Bs, H), device=dev)
+        d["out"] = torch.empty((L, Bs, H), dtype=torch.bfloat16, device=dev)
+        d["o"] = torch.empty((L, Bs, Hq, hd), dtype=torch.bfloat16, device=dev)
+        d["ws"] = torch.empty(sfa.enhance_workspace_size(L, 1, H), dtype=torch.uint8, device=dev)
+        return d
+
+    def fused(d):
+        sfa.decode_step_enhance(d["q"], d["k_new"], d["v_new"], d["ring_k"], d["ring_v"], d["state"], d["pos"],
+                                d["gamma"], d["alpha"], d["e_ring"], d["field"], d["prep"], out=d["out"])
+
+    def unfused(d):  # one sequence: its enhancement stream starts at its position
+        sfa.decode_step(d["q"], d["k_new"], d["v_new"], d["ring_k"], d["ring_v"], d["state"], d["pos"],
+                        d["gamma"], d["alpha"], out=d["o"])
+        sfa.enhance_prepared(d["o"].view(L, 1, H), d["prep"], d["e_ring"][:, 0], d["field"][:, 0],
+                             t0=int(d["pos0"]), out=d["out"].view(L, 1, H), workspace=d["ws"])
+
+    def per_call_us(fn, bufs):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for d in bufs:
+                fn(d)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for d in bufs:
+                fn(d)
+        for _ in range(3):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream(dev)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * len(bufs))
+
+    one = []
+    for i in range(sets):
+        d = make(1, 6000 + i)
+        d["pos0"] = int(d["pos"][0])
+        one.append(d)
+    us_fused = per_call_us(fused, one)
+    us_unfused = per_call_us(unfused, one)
+    del one
+    torch.cuda.empty_cache()
+    big = [make(256, 6100)]
+    us_big = per_call_us(fused, big)
+    del big
+    torch.cuda.empty_cache()
+    return {"workload": "7B-shaped decode step fused with the triple-channel enhancement, 28 layers, "
+                        "hidden 3584, 64-slot pool per layer, bf16",
+            "one_sequence": {"fused_us_per_step": us_fused, "unfused_us_per_step": us_unfused,
+                             "unfused": "sfa_decode_step + sfa_enhance_prepared (T = 1)"},
+            "batch_256_fused_us_per_step": us_big}
+
+
 def enhance_bytes(L=24, T=4096, H=1024, S=64, R=16):
     return L * T * H * 2 * 2 + L * S * H * 4 + 2 * L * R * H * 4 + 2 * L * H * 4
 
@@ -576,7 +653,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["c2", "decode", "enhance", "variants"], default=None,
+    ap.add_argument("--only", choices=["c2", "decode", "enhance", "decode_enhance", "variants"], default=None,
                     help="run only this secondary measurement (for profiling)")
     args = ap.parse_args()
 
@@ -591,7 +668,8 @@ def main():
         copy_calibration()
         return
     if args.only:
-        run = {"c2": run_c2, "decode": run_decode, "enhance": run_enhance, "variants": run_variants}[args.only]
+        run = {"c2": run_c2, "decode": run_decode, "enhance": run_enhance, "decode_enhance": run_decode_enhance,
+               "variants": run_variants}[args.only]
         print(json.dumps(run()), flush=True)
         return
 
@@ -621,6 +699,7 @@ def main():
         res["c2"] = run_c2()
         res["decode"] = run_decode()
         res["enhance"] = run_enhance()
+        res["decode_enhance"] = run_decode_enhance()
         res["variants"] = run_variants()
         res["copy_ceiling_gbps"] = copy_ceiling()
     if not args.no_cpu_baseline:

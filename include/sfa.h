@@ -372,6 +372,51 @@ int sfa_enhance_prepared(const void *attn, void *out, float *ring, float *field,
                          int in_dtype, int out_dtype,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * sfa_decode_step_enhance -- sfa_decode_step fused with the triple-channel
+ * enhancement of every (layer, sequence)'s attention output, which never
+ * leaves the chip (first page, sections 2.1-2.2, for the step; page "Dalin
+ * Soma SFA..." sections 2.1, 2.2 and 2.4 for the enhancement, applied per
+ * layer to each new token's attention output as the engine of page "Signal
+ * Field Attention (SFA)" does).
+ *
+ * For layer l (global index lg = layer0 + l) and sequence b with p = pos[b]:
+ * the decode step of sfa_decode_step (S per KV head) gives the attention row
+ * o (all Hq heads, H = Hq·d values); a = o as out_dtype holds it (rounded to
+ * bf16 for SFA_BF16); then, on that sequence's enhancement state,
+ *   e_ring[l,b][p mod R] <- a;  rm = Σ e_ring[l,b] / R
+ *   field[l,b] <- γ_e·field[l,b] + (1-γ_e)·a
+ *   c_j = <a, s_j> / (max(|a|,1e-12)·|s_j|),  w = softmax(c / T),  sem = Σ_j w_j·s_j
+ *   out[l,b] = a + α_lg·clip(rm + 0.5·field + 0.5·sem, -clip, +clip)
+ * with α_lg as in sfa_enhance.  This equals sfa_decode_step (out_dtype) then
+ * sfa_enhance of the one token at stream position p, per sequence.
+ *
+ *  q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha: as
+ *               sfa_decode_step (S per KV head).  A negative pos[b] skips
+ *               the sequence: nothing of it is written.
+ *  out          [L,B,H] out_dtype (written): the enhanced attention rows.
+ *  e_ring       [L,B,R,H] fp32, each sequence's last R attention rows
+ *               (slot p mod R), updated; zeros for a fresh stream.
+ *  field        [L,B,H] fp32, updated; zeros for a fresh stream.
+ *  prepared     pool records of sfa_enhance_prepare_pool for hidden size H:
+ *               shared_pool != 0: record 0 for every layer; otherwise layer
+ *               l of the call uses record l.  n_slots as prepared.
+ *  enhancement  [L,B,H] fp32 or NULL: α_lg·clip(...) (written when non-NULL).
+ *  Limits (else SFA_ERR_UNSUPPORTED): bf16 inputs, Hq/Hkv <= 16, H <= 4096.
+ *  One workgroup per (layer, sequence) reads its layer's pool: the form
+ *  suits the engine's shape (one sequence, every layer); a large batch
+ *  re-reads every pool once per sequence.
+ */
+int sfa_decode_step_enhance(const void *q, const void *k_new, const void *v_new,
+                            void *ring_k, void *ring_v, float *state,
+                            const int32_t *pos, const float *gamma, const float *alpha,
+                            void *out, float *e_ring, float *field,
+                            const void *prepared, int shared_pool, float *enhancement,
+                            int L, int B, int Hq, int Hkv, int d, int window, float scale,
+                            int layer0, int n_layers, float alpha_base, float cross_decay,
+                            float ema_gamma, float temperature, float clip, int ring_size,
+                            int n_slots, int in_dtype, int out_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -199,3 +199,46 @@ def enhance(attn, pool, ring=None, field=None, *, layer0: int = 0, n_layers: int
                            L, layer0, nl, T, H, t0, alpha_base, cross_decay, ema_gamma,
                            temperature, clip, ring_size, n_slots)
     return out, enh, R, F
+
+
+def decode_step_enhance(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, pool, e_ring, field, *,
+                        layer0: int = 0, n_layers: int | None = None, alpha_base: float = 0.1,
+                        cross_decay: float = 0.8, ema_gamma: float = 0.98, temperature: float = 0.07,
+                        clip: float = 0.5, shared_pool: bool = False, round_bf16: bool = True,
+                        scale: float = 0.0):
+    """The decode step followed, per sequence, by the triple-channel enhancement
+    of its new token ([P1] 2.1-2.2 for the step; [P3] 2.1-2.2, 2.4 for the
+    enhancement, applied per layer to each token's attention output as the
+    engine of [P2] does).  A composition of decode_step and enhance: no
+    arithmetic of its own beyond rounding the attention row to the step's
+    output dtype (bf16 with round_bf16, else fp32, as enhance reads it).
+
+    q [L,B,Hq,d] ... as decode_step (S per KV head); pool as enhance;
+    e_ring [L,B,R,H], field [L,B,H] each sequence's enhancement state, the new
+    token at stream position pos[b] (ring slot pos[b] mod R).  A negative
+    pos[b] leaves the sequence untouched.
+    Returns (out [L,B,H], enhancement [L,B,H], ring_k, ring_v, state, e_ring,
+    field) as float64 arrays.
+    """
+    o, rk, rv, st = decode_step(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, scale=scale)
+    L, B, Hq, d = o.shape
+    H = Hq * d
+    a = o.reshape(L, B, H)
+    if round_bf16:
+        import torch
+        a = torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).double().numpy()
+    er = _np(e_ring, np.float64).copy()
+    fd = _np(field, np.float64).copy()
+    out = np.zeros((L, B, H))
+    enh = np.zeros((L, B, H))
+    p = _np(pos, np.int32)
+    nl = layer0 + L if n_layers is None else n_layers
+    for b in range(B):
+        if p[b] < 0:
+            continue
+        ob, eb, rb, fb = enhance(a[:, b:b + 1], pool, er[:, b], fd[:, b], layer0=layer0,
+                                 n_layers=nl, t0=int(p[b]), alpha_base=alpha_base, cross_decay=cross_decay,
+                                 ema_gamma=ema_gamma, temperature=temperature, clip=clip,
+                                 ring_size=er.shape[2], shared_pool=shared_pool)
+        out[:, b], enh[:, b], er[:, b], fd[:, b] = ob[:, 0], eb[:, 0], rb, fb
+    return out, enh, rk, rv, st, er, fd

@@ -206,3 +206,22 @@ def test_enhance_pool_bytes():
     assert rec % 256 == 0 and rec >= 1024 * 64 * 4 * 2  # both operand orders, bf16 hi + lo
     assert lib.sfa_enhance_pool_bytes(24, 1024) == 24 * rec
     assert lib.sfa_enhance_pool_bytes(0, 1024) == 0
+
+
+def _decode_enhance(**kw):
+    args = dict(q=P, k_new=P, v_new=P, ring_k=P, ring_v=P, state=P, pos=P, gamma=P, alpha=P, out=P,
+                e_ring=P, field=P, prepared=P, shared=1, enh=None, L=1, B=1, Hq=2, Hkv=1, d=64, window=16,
+                scale=0.0, layer0=0, n_layers=1, alpha_base=0.1, cross_decay=0.8, ema_gamma=0.98,
+                temperature=0.07, clip=0.5, ring_size=16, n_slots=64, in_dtype=1, out_dtype=1, stream=None)
+    args.update(kw)
+    return _lib.lib().sfa_decode_step_enhance(*args.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(window=0), INV), (dict(ring_size=17), INV), (dict(n_slots=0), INV), (dict(temperature=0.0), INV),
+    (dict(layer0=1), INV), (dict(d=96), UNS), (dict(in_dtype=0), UNS), (dict(Hq=34, Hkv=2), UNS),
+    (dict(Hq=33, Hkv=1, d=128), UNS), (dict(prepared=None), INV), (dict(prepared=P + 16), INV),
+    (dict(e_ring=None), INV), (dict(field=P + 4), INV), (dict(L=0, q=None), OK), (dict(B=0, pos=None), OK),
+])
+def test_decode_step_enhance_rejects_before_launch(kw, want):
+    assert _decode_enhance(**kw) == want

@@ -756,3 +756,42 @@ def test_invalid_window_is_rejected_loudly():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                        timeout=120)
     assert r.returncode != 0 and "invalid argument" in r.stderr
+
+
+@pytest.mark.parametrize("rbf16", [True, False], ids=["bf16-row", "fp32-row"])
+def test_decode_step_enhance_equals_prefill_then_stream_enhance(rbf16):
+    """A prefill of n tokens followed by m fused decode-and-enhance steps gives,
+    token by token, what a prefill of n + m tokens followed by one enhancement
+    of the whole token stream gives (ring slot = stream position mod R, the
+    layer's α at global layer layer0 + l, both sequences independent)."""
+    B, Hq, Hkv, d, W, R, S, n, m = 2, 4, 2, 8, 4, 3, 5, 6, 5
+    H, N = Hq * d, n + m
+    q, k, v = _rand((B, N, Hq, d)), _rand((B, N, Hkv, d)), _rand((B, N, Hkv, d))
+    gamma, alpha = RNG.uniform(0.5, 0.99, Hkv), RNG.uniform(0, 0.5, Hq)
+    pool = _rand((S, H))
+    pool /= np.linalg.norm(pool, axis=1, keepdims=True)
+    kw = dict(alpha_base=0.8, cross_decay=0.9, ema_gamma=0.7, temperature=0.2, clip=0.6)
+
+    def rnd(x):
+        x = np.ascontiguousarray(x)
+        return torch.from_numpy(x).to(torch.bfloat16).double().numpy() if rbf16 else x.astype(np.float32)
+
+    full, *_ = oracle.prefill(q, k, v, gamma, alpha, W)
+    ref = [oracle.enhance(rnd(full[b].reshape(1, N, H)), pool, layer0=2, n_layers=5, ring_size=R,
+                          shared_pool=True, **kw)[0][0] for b in range(B)]
+    o, rk, rv, st = oracle.prefill(q[:, :n], k[:, :n], v[:, :n], gamma, alpha, W)
+    er = np.zeros((1, B, R, H))
+    fd = np.zeros((1, B, H))
+    for b in range(B):
+        _, _, rb, fb = oracle.enhance(rnd(o[b].reshape(1, n, H)), pool, layer0=2, n_layers=5, ring_size=R,
+                                      shared_pool=True, **kw)
+        er[0, b], fd[0, b] = rb[0], fb[0]
+    rk, rv, st = rk[None], rv[None], st[None]
+    for i in range(m):
+        t = n + i
+        out, _, rk, rv, st, er, fd = oracle.decode_step_enhance(
+            q[None, :, t], k[None, :, t], v[None, :, t], rk, rv, st, np.full(B, t, dtype=np.int32),
+            gamma[None], alpha[None], pool, er, fd, layer0=2, n_layers=5, shared_pool=True,
+            round_bf16=rbf16, **kw)
+        for b in range(B):
+            np.testing.assert_allclose(out[0, b], ref[b][t], rtol=1e-12, atol=1e-12)

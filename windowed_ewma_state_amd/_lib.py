@@ -20,7 +20,8 @@ SFA_PREFILL_SCAN, SFA_PREFILL_ATTEND, SFA_PREFILL_SINGLE_PASS = 1, 2, 4
 EXPORTS = ("sfa_status_string", "sfa_abi_version", "sfa_prefill_workspace_size", "sfa_prefill",
            "sfa_prefill_part", "sfa_prefill_qh", "sfa_prefill_rm", "sfa_prefill_noalloc",
            "sfa_decode_step", "sfa_decode_step_qh", "sfa_decode_step_rm", "sfa_enhance_workspace_size",
-           "sfa_enhance", "sfa_enhance_pool_bytes", "sfa_enhance_prepare_pool", "sfa_enhance_prepared")
+           "sfa_enhance", "sfa_enhance_pool_bytes", "sfa_enhance_prepare_pool", "sfa_enhance_prepared",
+           "sfa_decode_step_enhance")
 
 _lib = None
 
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
         L.sfa_enhance_prepared.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I,
                                            F, F, F, F, F, I, I, I, I, P, Z, P]
         L.sfa_enhance_prepared.restype = I
+        L.sfa_decode_step_enhance.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, I, P,
+                                              I, I, I, I, I, I, F, I, I, F, F, F, F, F, I, I, I, I, P]
+        L.sfa_decode_step_enhance.restype = I
         _lib = L
     return _lib
 

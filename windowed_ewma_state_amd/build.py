@@ -17,7 +17,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsfa.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["decode.hip", "prefill.hip", "enhance.hip", "sfa_api.cpp"]
+SOURCES = ["decode.hip", "decode_enhance.hip", "prefill.hip", "enhance.hip", "sfa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

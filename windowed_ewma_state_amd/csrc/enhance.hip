@@ -60,11 +60,6 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-__device__ __forceinline__ float alpha_layer(float base, float decay, int layer, int n_layers) {
-    const float ratio = n_layers > 1 ? (float)layer / (float)(n_layers - 1) : 0.f;
-    return base * (0.3f + 0.7f * ratio) * powf(decay, (float)layer);
-}
-
 __device__ __forceinline__ void split8(const float *v, uint16_t *hi, uint16_t *lo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

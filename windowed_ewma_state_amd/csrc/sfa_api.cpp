@@ -280,6 +280,55 @@ int sfa_decode_step_rm(const void *q, const void *k_new, const void *v_new, void
                        out, L, B, Hq, Hkv, d, window, scale, in_dtype, out_dtype, stream);
 }
 
+int sfa_decode_step_enhance(const void *q, const void *k_new, const void *v_new, void *ring_k, void *ring_v,
+                            float *state, const int32_t *pos, const float *gamma, const float *alpha,
+                            void *out, float *e_ring, float *field, const void *prepared, int shared_pool,
+                            float *enhancement, int L, int B, int Hq, int Hkv, int d, int window, float scale,
+                            int layer0, int n_layers, float alpha_base, float cross_decay, float ema_gamma,
+                            float temperature, float clip, int ring_size, int n_slots, int in_dtype,
+                            int out_dtype, void *stream) {
+    if (L < 0 || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return SFA_ERR_INVALID_ARG;
+    if (window < 1 || window > SFA_MAX_WINDOW) return SFA_ERR_INVALID_ARG;
+    if (ring_size < 1 || ring_size > SFA_MAX_WINDOW || n_slots < 1 || n_slots > 64) return SFA_ERR_INVALID_ARG;
+    if (!(temperature > 0.f) || !(clip >= 0.f) || layer0 < 0 || n_layers < 1 || n_layers < layer0 + L)
+        return SFA_ERR_INVALID_ARG;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return SFA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return SFA_ERR_UNSUPPORTED;
+    // the fused form: bf16 inputs, up to 16 query heads per KV head, a hidden
+    // row of at most 4096 (held in LDS)
+    if (in_dtype != SFA_BF16 || Hq / Hkv > 16 || (long long)Hq * d > 4096) return SFA_ERR_UNSUPPORTED;
+    if (L == 0 || B == 0) return SFA_OK;
+    if ((long long)L * B * Hkv >= (1LL << 31) / 64) return SFA_ERR_INVALID_ARG;
+    if ((long long)L * B * Hq >= (1LL << 31) / 128) return SFA_ERR_INVALID_ARG;
+    if ((long long)L * B * ring_size * Hq * d >= (1LL << 31)) return SFA_ERR_INVALID_ARG;  // ring offsets
+    if (!q || !k_new || !v_new || !ring_k || !ring_v || !state || !pos || !gamma || !alpha || !out || !e_ring ||
+        !field || !prepared)
+        return SFA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(ring_k, 16) ||
+        !aligned(ring_v, 16) || !aligned(state, 16) || !aligned(out, 16) || !aligned(e_ring, 16) ||
+        !aligned(field, 16) || !aligned(prepared, 256) || (enhancement && !aligned(enhancement, 16)))
+        return SFA_ERR_INVALID_ARG;
+    sfa::DecodeEnhanceArgs a{};
+    sfa::DecodeArgs &da = a.d;
+    da.q = q; da.k_new = k_new; da.v_new = v_new;
+    da.ring_k = ring_k; da.ring_v = ring_v; da.state = state;
+    da.pos = pos; da.gamma = gamma; da.alpha = alpha; da.out = out;
+    da.L = L; da.B = B; da.Hq = Hq; da.Hkv = Hkv; da.d = d; da.W = window; da.group = Hq / Hkv;
+    da.scale_log2e = scale_log2e(scale, d);
+    da.in_bf16 = 1;
+    da.out_bf16 = out_dtype == SFA_BF16;
+    da.s_per_query = 0;
+    da.running_mean = 0;
+    a.out = out; a.ring = e_ring; a.field = field; a.enhancement = enhancement;
+    a.pool_rec = static_cast<const unsigned char *>(prepared);
+    a.pool_rec_bytes = shared_pool ? 0 : sfa::pool_rec_bytes(Hq * d);
+    a.H = Hq * d; a.R = ring_size; a.n_slots = n_slots; a.layer0 = layer0; a.n_layers = n_layers;
+    a.alpha_base = alpha_base; a.cross_decay = cross_decay; a.ema_gamma = ema_gamma;
+    a.inv_temp_log2e = 1.4426950408889634f / temperature;
+    a.clip = clip;
+    return hip_status(sfa::launch_decode_enhance(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t sfa_enhance_workspace_size(int L, int T, int H) {
     if (L <= 0 || T <= 0 || H <= 0) return 0;
     return sfa::enhance_workspace_bytes(L, T, H, L);

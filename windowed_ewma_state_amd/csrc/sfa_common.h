@@ -44,6 +44,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// per-layer factor of the triple-channel enhancement: α_base·(0.3 + 0.7·l/(L-1))·decay^l
+// (page "Dalin Soma SFA..." section 2.2; ratio 0 for a single layer)
+__device__ __forceinline__ float alpha_layer(float base, float decay, int layer, int n_layers) {
+    const float ratio = n_layers > 1 ? (float)layer / (float)(n_layers - 1) : 0.f;
+    return base * (0.3f + 0.7f * ratio) * powf(decay, (float)layer);
+}
+
 // ---- cross-lane reductions over the four 16-lane groups (l ^ 16, l ^ 32) ----
 __device__ __forceinline__ float max_over_groups(float x) {
     x = fmaxf(x, __shfl_xor(x, 16));

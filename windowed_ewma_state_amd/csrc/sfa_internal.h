@@ -102,6 +102,21 @@ size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers);
 hipError_t launch_enhance(const EnhanceArgs &a, hipStream_t stream);
 hipError_t launch_pool_prepare(const EnhanceArgs &a, hipStream_t stream);
 
+// the decode step fused with the triple-channel enhancement of each
+// (layer, sequence)'s attention row (hidden H = Hq·d)
+struct DecodeEnhanceArgs {
+    DecodeArgs d;            // the decode step (its out is not used)
+    void *out;               // [L,B,H] out_dtype: a + α_l·clip(e)
+    float *ring;             // [L,B,R,H] the last R attention rows of the sequence (slot pos mod R)
+    float *field;            // [L,B,H]
+    float *enhancement;      // [L,B,H] α_l·clip(e), or null
+    const unsigned char *pool_rec;  // prepared pool records (1/|s| and the bf16 hi/lo operand tables)
+    long long pool_rec_bytes;       // stride between layers' records (0: one shared record)
+    int H, R, n_slots, layer0, n_layers;
+    float alpha_base, cross_decay, ema_gamma, inv_temp_log2e, clip;
+};
+hipError_t launch_decode_enhance(const DecodeEnhanceArgs &a, hipStream_t stream);
+
 // XCD-aware block remap: consecutive logical indices land on the same XCD
 // (hardware dispatches workgroups round-robin over the 8 XCDs of an MI355X).
 __device__ __forceinline__ int xcd_remap(int bid, int nblk) {

@@ -337,3 +337,48 @@ def enhance_prepared(attn, prepared: PreparedPool, ring, field, *, layer0: int =
         _stream(stream, dev))
     _lib.check(st, "sfa_enhance_prepared")
     return out, enhancement
+
+
+@_on_call_stream
+def decode_step_enhance(q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha, e_ring, field,
+                        prepared: PreparedPool, *, layer0: int = 0, n_layers: int | None = None,
+                        alpha_base: float = 0.1, cross_decay: float = 0.8, ema_gamma: float = 0.98,
+                        temperature: float = 0.07, clip: float = 0.5, scale: float = 0.0, out=None,
+                        out_dtype=None, enhancement=None, stream=None):
+    """sfa_decode_step_enhance: the decode step of decode_step (S per KV head)
+    with each (layer, sequence)'s attention row enhanced on chip.  e_ring
+    [L,B,R,H] and field [L,B,H] fp32 (the enhancement state of every
+    sequence, updated in place), prepared: enhance_prepare_pool of the pool
+    (record l for layer l of the call, or a shared one).  Returns out [L,B,H]."""
+    L, B, Hq, d = q.shape
+    Hkv = k_new.shape[2]
+    H = Hq * d
+    W = ring_k.shape[3]
+    R = e_ring.shape[2]
+    dev = q.device
+    if prepared.H != H:
+        raise ValueError(f"pool prepared for hidden size {prepared.H}, the attention row has {H}")
+    if not prepared.shared and prepared.n_layers < L:
+        raise ValueError(f"{prepared.n_layers} prepared pool layers for a call over {L} layers")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((L, B, H), dtype=out_dtype, device=dev)
+    g = _vec(gamma, L * Hkv, dev, "gamma")
+    a = _vec(alpha, L * Hq, dev, "alpha")
+    nl = layer0 + L if n_layers is None else n_layers
+    st = _lib.lib().sfa_decode_step_enhance(
+        _dev(q, "q", q.dtype, (L, B, Hq, d), dev), _dev(k_new, "k_new", q.dtype, (L, B, Hkv, d), dev),
+        _dev(v_new, "v_new", q.dtype, (L, B, Hkv, d), dev),
+        _dev(ring_k, "ring_k", q.dtype, (L, B, Hkv, W, d), dev),
+        _dev(ring_v, "ring_v", q.dtype, (L, B, Hkv, W, d), dev),
+        _dev(state, "state", torch.float32, (L, B, Hkv, d), dev),
+        _dev(pos, "pos", torch.int32, (B,), dev), _dev(g, "gamma"), _dev(a, "alpha"),
+        _dev(out, "out", None, (L, B, H), dev),
+        _dev(e_ring, "e_ring", torch.float32, (L, B, R, H), dev), _dev(field, "field", torch.float32, (L, B, H), dev),
+        _dev(prepared.buf, "prepared"), int(prepared.shared),
+        _dev(enhancement, "enhancement", torch.float32, (L, B, H), dev),
+        L, B, Hq, Hkv, d, W, float(scale), layer0, nl, float(alpha_base), float(cross_decay),
+        float(ema_gamma), float(temperature), float(clip), R, prepared.n_slots, _dtype_code(q, "q"),
+        _dtype_code(out, "out"), _stream(stream, dev))
+    _lib.check(st, "sfa_decode_step_enhance")
+    return out

@@ -588,18 +588,25 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     const TIn *Ag = reinterpret_cast<const TIn *>(a.attn) + (long)l * T * H;
 
     // ---- (1) loads: staging items, the operand table, pool^T, field carry ----
+    // (rows past the end and columns past H read a clamped valid piece: they
+    // only feed outputs that are never stored; rows before the stream start,
+    // in the call's first tile only, must contribute zero to the band)
     u32x4 stg[NIT][RPI];
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
         const int it = threadIdx.x + 256 * k;
         if (it < NITEM) {
             const int rq = it / CPR, cp = it % CPR;
-            const int col = xb + cp * EPC;
+            const int col = min(xb + cp * EPC, H - EPC);
 #pragma unroll
             for (int i = 0; i < RPI; ++i) {
-                const int t = tb - kBlk + RPI * rq + i;
-                stg[k][i] = u32x4{0u, 0u, 0u, 0u};
-                if (t >= 0 && t < T && col < H) stg[k][i] = *reinterpret_cast<const u32x4 *>(Ag + (long)t * H + col);
+                const int t = min(max(tb - kBlk + RPI * rq + i, 0), T - 1);
+                stg[k][i] = *reinterpret_cast<const u32x4 *>(Ag + (long)t * H + col);
+            }
+            if (tb < kBlk) {  // the first tile: zero the rows before the stream start
+#pragma unroll
+                for (int i = 0; i < RPI; ++i)
+                    if (tb - kBlk + RPI * rq + i < 0) stg[k][i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     }

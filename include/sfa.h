@@ -326,6 +326,13 @@ size_t sfa_enhance_workspace_size(int L, int T, int H);
  *  enhancement  [L,T,H] fp32 or NULL: enh values (written when non-NULL).
  *  R = ring_size in [1,16]; n_slots in [1,64]; temperature > 0; clip >= 0.
  *  workspace:   at least sfa_enhance_workspace_size(L, T, H) bytes.
+ *
+ * Precision: the contractions run on bf16 MFMAs with fp32 accumulation; bf16
+ * attention values enter exactly, fp32 ones and every other operand as bf16
+ * hi + lo pairs (about 2^-17 relative).  Exception, bf16 inputs only: a layer
+ * whose α_lg·0.5·(2^-8 + 2^-18)·max|s| (max over that layer's pool entries)
+ * is at most 1e-5 takes the pool and the slot weights of its semantic sum as
+ * single bf16 values, which moves its outputs by at most that bound.
  */
 int sfa_enhance(const void *attn, void *out, float *ring, float *field,
                 const float *pool, long long pool_layer_stride, float *enhancement,
@@ -389,7 +396,8 @@ int sfa_enhance_prepared(const void *attn, void *out, float *ring, float *field,
  *   c_j = <a, s_j> / (max(|a|,1e-12)·|s_j|),  w = softmax(c / T),  sem = Σ_j w_j·s_j
  *   out[l,b] = a + α_lg·clip(rm + 0.5·field + 0.5·sem, -clip, +clip)
  * with α_lg as in sfa_enhance.  This equals sfa_decode_step (out_dtype) then
- * sfa_enhance of the one token at stream position p, per sequence.
+ * sfa_enhance of the one token at stream position p, per sequence (here the
+ * semantic operands are always bf16 hi + lo pairs).
  *
  *  q, k_new, v_new, ring_k, ring_v, state, pos, gamma, alpha: as
  *               sfa_decode_step (S per KV head).  A negative pos[b] skips

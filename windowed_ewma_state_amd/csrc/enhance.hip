@@ -48,6 +48,14 @@ constexpr int kOpElems = 64 * 8;   // one MFMA operand (64 lanes x 8 bf16)
 constexpr int kAggMaxH = 8192;     // hidden sizes whose field aggregate k_sem computes
 constexpr int kCoefEnt = 8;        // (token group, k-step) pairs of the band/field operand
 constexpr int kTabEntries = kCoefEnt * 2 * 64;  // band/field operands (u32x4)
+// Single-bf16 semantic operands.  With x = hi(x)·(1+ε), |ε| <= 2^-9, the product
+// of the rounded weight 0.5·w_s and the rounded slot entry s_sx is off by at
+// most (2^-8 + 2^-18)·0.5·w_s·|s_sx|; the weights sum to one, so the semantic
+// term 0.5·sem_x moves by at most 0.5·(2^-8 + 2^-18)·max|s|, and clip (1-
+// Lipschitz) and α_l carry that to the output.  A layer takes the single
+// operands when α_l times that is at most kSemSingleBound.
+constexpr float kSemSingleErr = 0.5f * (0x1p-8f + 0x1p-18f);
+constexpr float kSemSingleBound = 1e-5f;
 // workgroups that write the band/field operand table and α of each layer
 __host__ __device__ inline int kCallTableBlocks(const EnhanceArgs &a) { return kTabEntries / 256 + (a.L + 255) / 256; }
 
@@ -552,8 +560,17 @@ __device__ __forceinline__ float band_field_coef(int t, int j, int R, float g) {
     return c;
 }
 
+// the staged tile, and at the end the output tile (row-major, 16-byte padded rows)
 template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
+constexpr int cols_lds_bytes() {
+    return kCB * ColLayout<TIn>::kColBytes > kTile * (kCB * (int)sizeof(TOut) + 16)
+               ? kCB * ColLayout<TIn>::kColBytes : kTile * (kCB * (int)sizeof(TOut) + 16);
+}
+
+// one (layer, tile, column block); kSemLo: the semantic operands (pool^T and
+// the slot weights) as bf16 hi + lo pairs, else as bf16 hi alone
+template <typename TIn, typename TOut, bool kSemLo>
+__device__ __forceinline__ void cols_block(const EnhanceArgs &a, int lid, unsigned char *AsT, u32x4 *TabS) {
     constexpr bool kPrecise = std::is_same<TIn, float>::value;  // fp32 inputs: split a
     using LY = ColLayout<TIn>;
     constexpr int kRowsE = kBlk + kTile;     // staged tokens tb-16 .. tb+63
@@ -566,14 +583,8 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     static_assert(NTAB % 256 == 0, "table copy must split evenly");
     constexpr int kSteps[4] = {1, 2, 2, 3}, kIdStep[4] = {0, 1, 1, 2};
     constexpr int OW = 2 * (int)sizeof(TOut);  // output dwords per 8 values
-    // the staged tile, and at the end the output tile (row-major, 16-byte padded rows)
-    constexpr int kAsBytes = kCB * LY::kColBytes > kTile * (kCB * (int)sizeof(TOut) + 16)
-                                 ? kCB * LY::kColBytes : kTile * (kCB * (int)sizeof(TOut) + 16);
-    __shared__ __attribute__((aligned(16))) unsigned char AsT[kAsBytes];
-    __shared__ __attribute__((aligned(16))) u32x4 TabS[NTAB];
 
     const int ncb = (a.H + kCB - 1) / kCB;
-    const int lid = xcd_remap(blockIdx.x, a.L * a.ntiles * ncb);
     const int cb = lid % ncb, lt = lid / ncb;  // lt = layer * ntiles + tile
     const int l = lt / a.ntiles, tile = lt % a.ntiles;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -615,7 +626,7 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
     for (int k = 0; k < NTAB / 256; ++k) tab[k] = reinterpret_cast<const u32x4 *>(a.coef)[threadIdx.x + 256 * k];
     const int pl = a.n_pool_layers == 1 ? 0 : l;
     const uint16_t *poolT = rec_poolT(a, pl) + lane * 8;
-    constexpr int SL = 2;  // the semantic operands as bf16 hi + lo
+    constexpr int SL = kSemLo ? 2 : 1;  // the semantic operands as bf16 hi (+ lo)
     bf16x8 pt[2][2][SL];  // [half][slot k-step][hi/lo]
     float Fc[8];
     if (has) {
@@ -737,15 +748,17 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
                     if constexpr (kPrecise) D[h] = mfma_bf16_16x16x32(Al[st][h], ch_, D[h]);
                 }
             }
-            // 0.5·semantic: pool^T · (0.5 w)^T, both split into bf16 hi + lo
+            // 0.5·semantic: pool^T · (0.5 w)^T (hi·hi + hi·lo + lo·hi with the pairs)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const bf16x8 *w = wb[tg & 1][ks];
                     D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[0], D[h]);
-                    D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[1], D[h]);
-                    D[h] = mfma_bf16_16x16x32(pt[h][ks][1], w[0], D[h]);
+                    if constexpr (kSemLo) {
+                        D[h] = mfma_bf16_16x16x32(pt[h][ks][0], w[1], D[h]);
+                        D[h] = mfma_bf16_16x16x32(pt[h][ks][1], w[0], D[h]);
+                    }
                 }
             }
             if (tg + 2 < 4) {  // every tile has all four groups' weights
@@ -837,7 +850,21 @@ __global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
         if (col < H)
             st_stream(Og + (long)(tb + r) * H + col, *reinterpret_cast<const u32x4 *>(AsT + r * ORB + 16 * pc));
     }
+}
 
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(256, 2) void k_cols(EnhanceArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char AsT[cols_lds_bytes<TIn, TOut>()];
+    __shared__ __attribute__((aligned(16))) u32x4 TabS[kTabEntries];
+    const int ncb = (a.H + kCB - 1) / kCB;
+    const int lid = xcd_remap(blockIdx.x, a.L * a.ntiles * ncb);
+    if constexpr (std::is_same<TIn, float>::value) {
+        cols_block<TIn, TOut, true>(a, lid, AsT, TabS);
+    } else {
+        const int l = lid / ncb / a.ntiles;
+        if (load_uniform(a.alpha_tab + a.L + l) != 0.f) cols_block<TIn, TOut, false>(a, lid, AsT, TabS);
+        else cols_block<TIn, TOut, true>(a, lid, AsT, TabS);
+    }
 }
 
 // last min(R, T) attention rows -> ring slots (t0 + t) mod R; one workgroup
@@ -859,7 +886,16 @@ __device__ void ring_write_block(const EnhanceArgs &a, int bid) {
 __device__ void call_tables_block(const EnhanceArgs &a, int bid) {
     if (bid >= kTabEntries / 256) {
         const int l = (bid - kTabEntries / 256) * 256 + threadIdx.x;
-        if (l < a.L) a.alpha_tab[l] = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
+        if (l < a.L) {
+            const float al = alpha_layer(a.alpha_base, a.cross_decay, a.layer0 + l, a.n_layers);
+            a.alpha_tab[l] = al;
+            // bf16 inputs: the semantic operands as single bf16 values where that
+            // moves the layer's outputs by at most kSemSingleBound (see below)
+            const float *smax = reinterpret_cast<const float *>(pool_rec(a, a.n_pool_layers == 1 ? 0 : l)) + kSlots;
+            float m = 0.f;
+            for (int s = 0; s < a.n_slots; ++s) m = fmaxf(m, smax[s]);
+            a.alpha_tab[a.L + l] = a.in_bf16 && fabsf(al) * kSemSingleErr * m <= kSemSingleBound ? 1.f : 0.f;
+        }
         return;
     }
     const int idx = bid * 256 + threadIdx.x;
@@ -942,8 +978,8 @@ size_t enhance_workspace_bytes(int L, int T, int H, int n_pool_layers) {
     // semantic weights: per tile 4 token groups x 2 k-steps x hi/lo x 512 bf16;
     // the band/field operand table
     const size_t wsem = (size_t)L * nt * 4 * 4 * kOpElems + (size_t)kTabEntries * 8;
-    // α per layer, rounded up to 64 floats
-    const size_t alphas = ((size_t)L + 63) / 64 * 64;
+    // α per layer and the per-layer semantic-operand choice, rounded up to 64 floats
+    const size_t alphas = (2 * (size_t)L + 63) / 64 * 64;
     return recs + (floats + alphas) * sizeof(float) + wsem * sizeof(uint16_t);
 }
 

@@ -120,7 +120,10 @@ __global__ __launch_bounds__(kDeThreads) void k_decode_enhance(DecodeEnhanceArgs
     __shared__ __attribute__((aligned(16))) float wsl[kDeSlots];  // 0.5·softmax weights
 
     const DecodeArgs &da = a.d;
-    const int lb = blockIdx.x;  // layer · B + sequence
+    // layer · B + sequence, XCD-aware: each XCD takes a contiguous run of
+    // (layer, sequence) pairs, so the sequences of one layer share that XCD's
+    // L2 copy of the layer's pool records
+    const int lb = xcd_remap(blockIdx.x, da.L * da.B);
     const int l = lb / da.B, b = lb % da.B;
     const int p = load_uniform(da.pos + b);
     if (p < 0) return;  // a skipped sequence: nothing of it is written

@@ -140,6 +140,10 @@ int sfa_prefill(const void *q, const void *k, const void *v,
  *                       (reads the carries from the workspace), and the ring
  *                       hand-off.  Must run after SCAN with the same arguments
  *                       and workspace, on the same stream (or ordered after it).
+ *   With bf16 inputs, S per KV head and at most 64 chunks per sequence the
+ *   carries are folded instead: SCAN writes the chunk aggregates and the S
+ *   before the call, and ATTEND composes each chunk's carry from them and
+ *   writes the final S into `state` (one launch fewer, same results).
  * parts = SCAN | ATTEND is exactly sfa_prefill.
  *   SFA_PREFILL_SINGLE_PASS  the whole call in one pass over the inputs (no
  *                       scan launches, K read once): every attention

@@ -148,3 +148,50 @@ def test_prefill_two_chunks_equal_one():
     check_exact(rk, ref[1], "ring_k")
     check_exact(rv, ref[2], "ring_v")
     check_state(st, ref[3])
+
+
+@pytest.mark.parametrize("n", [1000, 4096, 4096 + 29], ids=["n1000", "n4096", "n4125"])
+def test_prefill_parts_in_two_calls_equal_one(n):
+    """sfa_prefill_part: SCAN, then ATTEND in a second call on the same
+    workspace, equals one SCAN | ATTEND call bit for bit (out, ring, final S),
+    fresh and continued (per-sequence positions), on both sides of the 64-chunk
+    limit of the folded carries; and against the oracle."""
+    B, Hq, Hkv, hd, W = 2, 6, 2, 64, 16
+    d = inputs.prefill_inputs(B, n, Hq, Hkv, hd, seed=n + 7)
+    hist = [0, 37]
+    rk0 = inputs.normal((B, Hkv, W, hd), 901, 1.0, torch.bfloat16)
+    rv0 = inputs.normal((B, Hkv, W, hd), 902, 1.0, torch.bfloat16)
+    st0 = inputs.normal((B, Hkv, hd), 903, 1.0, torch.float32)
+    c = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ws = torch.empty(sfa.prefill_workspace_size(B, n, Hkv, hd), dtype=torch.uint8, device="cuda")
+    for cont in (False, True):
+        log(f"prefill parts in two calls, n={n}, continued={cont}")
+        res = []
+        for split in (False, True):
+            kw = dict(window=W, out_dtype=torch.float32, workspace=ws)
+            if cont:
+                kw.update(ring_k=rk0.cuda(), ring_v=rv0.cuda(), state=st0.cuda(),
+                          pos0=torch.tensor(hist, dtype=torch.int32, device="cuda"))
+            else:
+                kw.update(ring_k=torch.zeros_like(rk0).cuda(), ring_v=torch.zeros_like(rv0).cuda(),
+                          state=torch.zeros_like(st0).cuda())
+            if split:
+                out = torch.empty((B, n, Hq, hd), dtype=torch.float32, device="cuda")
+                sfa.prefill(c["q"], c["k"], c["v"], c["gamma"], c["alpha"], out=out, parts=1, **kw)
+                r = sfa.prefill(c["q"], c["k"], c["v"], c["gamma"], c["alpha"], out=out, parts=2, **kw)
+            else:
+                r = sfa.prefill(c["q"], c["k"], c["v"], c["gamma"], c["alpha"], **kw)
+            torch.cuda.synchronize()
+            res.append([t.clone() for t in r])
+        for a_, b_, name in zip(res[0], res[1], ("out", "ring_k", "ring_v", "state")):
+            assert torch.equal(a_, b_), name
+        if cont:
+            ref = oracle.prefill(d["q"], d["k"], d["v"], d["gamma"], d["alpha"], W, ring_k=rk0.float().numpy(),
+                                 ring_v=rv0.float().numpy(), state=st0.double().numpy(),
+                                 pos0=torch.tensor(hist, dtype=torch.int32))
+        else:
+            ref = oracle.prefill(d["q"], d["k"], d["v"], d["gamma"], d["alpha"], W)
+        check_output(res[0][0], ref[0], True, "out")
+        check_exact(res[0][1], ref[1], "ring_k")
+        check_exact(res[0][2], ref[2], "ring_v")
+        check_state(res[0][3], ref[3])

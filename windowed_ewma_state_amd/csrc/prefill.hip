@@ -21,6 +21,12 @@
 // A fourth, tiny launch copies the last W keys/values into the ring when the
 // call continues an existing cache (the first tile reads the old ring).
 //
+// Folded carries (S per KV head, bf16 inputs, at most 64 tiles per sequence;
+// chosen by the library for such calls): k_ewma_agg also writes the first
+// tile's carry (S before the call), k_ewma_carry does not run, and every
+// k_window_attn<.., FOLD> workgroup folds the aggregates of the tiles before
+// it onto that carry; the last tile writes the final S.
+//
 // Single pass (on request; S per KV head, bf16 inputs, at most 64 tiles per
 // sequence):
 //   k_fused_init  clears the published-aggregate words, saves the carried S;
@@ -117,6 +123,13 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     __shared__ float blkv[4][4][D];  // [wave][block][d]
     __shared__ float blkc[RM ? 4 : 1][4][RM ? D : 1];
     __shared__ float decay[4][4], beta[4][4];
+    if constexpr (!RM && !QH) {
+        if (a.fold && tile == 0) {  // the first tile's carry: S before the call
+            const long bgs = (long)b * a.Hkv + G;
+            float *c0p = a.carry + bgs * a.ntiles * D;
+            for (int e = lane; e < D; e += 64) c0p[e] = (a.pos0 && p0 > 0) ? a.state[bgs * D + e] : 0.f;
+        }
+    }
     for (int jh = 0; jh < nh; ++jh) {
     const int hs = QH ? G * a.group + jh : G;  // the scan chain's S head
     const int bg = b * a.Hs + hs;
@@ -442,7 +455,7 @@ __device__ __forceinline__ void fused_carry(const PrefillArgs &a, int bg, int ti
     }
     constexpr int kPer = (kFusedMaxTiles + 3) / 4;  // earlier tiles per wave, at most
     const int per = (tile + 3) / 4;
-    const int j0 = min(wave * per, tile), j1 = min(j0 + per, tile);
+    const int j0 = min(__builtin_amdgcn_readfirstlane(wave) * per, tile), j1 = min(j0 + per, tile);
     uint64_t v[kPer][EPL];
     bool ready = false;
     for (int it = 0; it < kSpinLimit && !ready; ++it) {
@@ -461,13 +474,16 @@ __device__ __forceinline__ void fused_carry(const PrefillArgs &a, int bg, int ti
         }
         ready = __builtin_amdgcn_ballot_w64(!ok) == 0;  // every lane's words published
     }
+    // (an earlier tile is whole; only the first can evict fewer than 64 keys,
+    // since W <= 16: the others all decay by γ^64)
+    const float g64 = powi(gm, kTile), gfirst = tile_decay(0);
     float X[EPL], G = 1.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) X[e] = 0.f;
 #pragma unroll
     for (int jj = 0; jj < kPer; ++jj) {
         if (j0 + jj < j1) {
-            const float g = tile_decay(j0 + jj);
+            const float g = j0 + jj == 0 ? gfirst : g64;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) X[e] = g * X[e] + __uint_as_float((uint32_t)v[jj][e]);
             G *= g;
@@ -550,7 +566,7 @@ __device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float *v) {
 // RM: the running mean of the keys that have left the window is the EWMA
 // input; the wave starts from the tile's carried (S, C) and the block
 // aggregates of its earlier blocks, then scans C += k, S = γS + (1-γ)·C/m.
-template <typename TIn, typename TOut, int D, int MODE, bool FUSED = false>
+template <typename TIn, typename TOut, int D, int MODE, bool FUSED = false, bool FOLD = false>
 __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     constexpr bool QH = MODE == kQueryHead, RM = MODE == kRunningMean;
     constexpr bool kBf16 = std::is_same<TIn, __bf16>::value;
@@ -567,12 +583,13 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // scan over the wave's 16 tokens); the LDS slot then only carries S at the
     // block start.  The other modes keep each token's S row in LDS.
     constexpr bool kRegS = !QH && !RM && kBf16;
-    static_assert(!FUSED || kRegS, "the single-pass form exists for S per KV head with bf16 inputs");
+    static_assert(!(FUSED || FOLD) || kRegS, "the single-pass and folded forms exist for S per KV head with bf16 inputs");
+    static_assert(!(FUSED && FOLD), "one carry form at a time");
     __shared__ __attribute__((aligned(16))) float Sb[4][kRegS ? D : kBlk * SS];
     // kRegS: each wave's block aggregate (the EWMA of its 16 tokens from zero);
     // single pass: the waves' partial folds of the earlier tiles' aggregates
     __shared__ __attribute__((aligned(16))) float BlkAgg[kRegS ? 4 : 1][kRegS ? D : 1];
-    __shared__ __attribute__((aligned(16))) float FoldX[FUSED ? 4 : 1][FUSED ? D : 1];
+    __shared__ __attribute__((aligned(16))) float FoldX[FUSED || FOLD ? 4 : 1][FUSED || FOLD ? D : 1];
     __shared__ float FoldG[4];
 
     const int nblk = a.B * a.Hkv * a.ntiles;
@@ -648,13 +665,30 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // QH: chain of query head h of this group
     const long chain0 = QH ? (long)b * a.Hq + (long)G * group : (long)bg;
     float Cin[EPL], Ain[kRegS ? 1 : 3][EPL];
+    // FOLD: wave w folds the earlier tiles [fj0, fj1) (a quarter of them); their
+    // aggregates are loaded here, unconditionally (a clamped index past the
+    // range), so the waits for these loads are counted exactly
+    constexpr int kFoldPer = FOLD ? (kFusedMaxTiles + 3) / 4 : 1;
+    float foldv[kFoldPer][FOLD ? EPL : 1];
+    const int fper = (tile + 3) / 4;
+    const int fj0 = min(__builtin_amdgcn_readfirstlane(wave) * fper, tile), fj1 = min(fj0 + fper, tile);
     if constexpr (kRegS) {
         // the block aggregates come from this tile's own scan (step 3); the
-        // single pass folds the earlier tiles' aggregates instead of a carry
+        // single pass folds the earlier tiles' aggregates instead of a carry,
+        // and the folded form folds them onto the first tile's carry
         if constexpr (!FUSED) {
-            const float *C = a.carry + (chain0 * a.ntiles + tile) * D + e0;
+            const float *C = a.carry + (chain0 * a.ntiles + (FOLD ? 0 : tile)) * D + e0;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) Cin[e] = C[e];
+        }
+        if constexpr (FOLD) {
+            const float *A64 = a.agg64 + chain0 * a.ntiles * D + e0;
+#pragma unroll
+            for (int jj = 0; jj < kFoldPer; ++jj) {
+                const int j = min(fj0 + jj, a.ntiles - 1);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) foldv[jj][e] = A64[(long)j * D + e];
+            }
         }
     } else {
         carry_loads(chain0, Cin, Ain);
@@ -904,6 +938,35 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
         float C[EPL];
         if constexpr (FUSED) {
             fused_carry<D, EPL>(a, bg, tile, p0, gm, wave, lane, e0, BlkAgg, FoldX, FoldG, C);
+        } else if constexpr (FOLD) {
+            // (Γ_w, X_w) of this wave's range, then C = the first tile's carry
+            // composed with the four ranges in order
+            // (an earlier tile is whole; only the first can evict fewer than
+            // 64 keys, since W <= 16: the others all decay by γ^64)
+            const float g64 = powi(gm, kTile);
+            const float gfirst = powi(gm, evict_steps(p0, 0, kTile, W));
+            float X[EPL], Gr = 1.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) X[e] = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < kFoldPer; ++jj) {
+                if (fj0 + jj < fj1) {
+                    const float g = fj0 + jj == 0 ? gfirst : g64;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) X[e] = g * X[e] + foldv[jj][e];
+                    Gr *= g;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) FoldX[wave][e0 + e] = X[e];
+            if (lane == 0) FoldG[wave] = Gr;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) C[e] = Cin[e];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) C[e] = FoldG[w] * C[e] + FoldX[w][e0 + e];
         } else {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) C[e] = Cin[e];
@@ -929,9 +992,9 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Sreg[k][half][i] = fmaf(Ac, s0[i], Sreg[k][half][i]);
             }
-        if constexpr (FUSED) {
-            // the single pass writes S after the last token: lanes c16 = 15 of
-            // the last wave (tokens past the end leave S unchanged)
+        if constexpr (FUSED || FOLD) {
+            // the single pass and the folded form write S after the last token:
+            // lanes c16 = 15 of the last wave (tokens past the end leave S unchanged)
             if (tile == a.ntiles - 1 && wave == 3 && c16 == kBlk - 1 && a.state) {
                 float *st = a.state + (long)bg * D;
 #pragma unroll
@@ -1219,6 +1282,23 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t stream, int parts) {
                 hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
             return hipGetLastError();
         }
+    }
+    // folded carries: S per KV head, bf16 inputs, at most kFusedMaxTiles tiles
+    PrefillArgs af = a;
+    af.fold = std::is_same<TIn, __bf16>::value && !a.s_per_query && !a.running_mean && a.ntiles <= kFusedMaxTiles;
+    if (af.fold) {
+        if constexpr (std::is_same<TIn, __bf16>::value) {
+            if (parts & kPrefillScan)
+                hipLaunchKernelGGL((k_ewma_agg<TIn, D, false, false>), dim3((tiles + 3) / 4), dim3(256), 0, stream,
+                                   af);
+            if (parts & kPrefillAttend) {
+                hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kKvHead, false, true>), dim3(tiles), dim3(256), 0,
+                                   stream, af);
+                if (a.pos0 && a.ring_k)
+                    hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, af);
+            }
+        }
+        return hipGetLastError();
     }
     if (parts & kPrefillScan) {
         // one wave per (tile, b, KV head); per query head it feeds the group's chains

@@ -61,6 +61,11 @@ struct PrefillArgs {
     // aggregate as tagged words and folds those of the tiles before it
     uint64_t *tagged;  // [B*Hkv][ntiles][d]  (fp32 bits, tag in the high word)
     float *sinit;      // [B*Hkv][d]          S carried into the call (0 for a fresh sequence)
+    // folded carries (S per KV head, bf16 inputs, at most kFusedMaxTiles tiles):
+    // the scan writes the tile aggregates and, as the first tile's carry, S
+    // before the call; each attention workgroup folds the earlier tiles'
+    // aggregates onto it (no carry launch) and the last tile writes the final S
+    int fold;
 };
 constexpr int kFusedMaxTiles = 64;
 size_t prefill_workspace_bytes(int B, int n, int Hkv, int d);

@@ -1305,25 +1305,25 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t stream, int parts) {
         const unsigned scan_tiles = (unsigned)(a.B * a.Hkv * a.ntiles);
         const dim3 agg_grid((scan_tiles + 3) / 4), carry_grid(a.B * a.Hs * (D / kCarryCols));
         if (a.running_mean) {
-            hipLaunchKernelGGL((k_ewma_agg<TIn, D, true, false>), agg_grid, dim3(256), 0, stream, a);
-            hipLaunchKernelGGL(k_ewma_carry<true>, carry_grid, dim3(1024), 0, stream, a);
+            hipLaunchKernelGGL((k_ewma_agg<TIn, D, true, false>), agg_grid, dim3(256), 0, stream, af);
+            hipLaunchKernelGGL(k_ewma_carry<true>, carry_grid, dim3(1024), 0, stream, af);
         } else {
             if (a.s_per_query)
-                hipLaunchKernelGGL((k_ewma_agg<TIn, D, false, true>), agg_grid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((k_ewma_agg<TIn, D, false, true>), agg_grid, dim3(256), 0, stream, af);
             else
-                hipLaunchKernelGGL((k_ewma_agg<TIn, D, false, false>), agg_grid, dim3(256), 0, stream, a);
-            hipLaunchKernelGGL(k_ewma_carry<false>, carry_grid, dim3(1024), 0, stream, a);
+                hipLaunchKernelGGL((k_ewma_agg<TIn, D, false, false>), agg_grid, dim3(256), 0, stream, af);
+            hipLaunchKernelGGL(k_ewma_carry<false>, carry_grid, dim3(1024), 0, stream, af);
         }
     }
     if (parts & kPrefillAttend) {
         if (a.s_per_query)
-            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kQueryHead>), dim3(tiles), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kQueryHead>), dim3(tiles), dim3(256), 0, stream, af);
         else if (a.running_mean)
-            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kRunningMean>), dim3(tiles), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kRunningMean>), dim3(tiles), dim3(256), 0, stream, af);
         else
-            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kKvHead>), dim3(tiles), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_window_attn<TIn, TOut, D, kKvHead>), dim3(tiles), dim3(256), 0, stream, af);
         if (a.pos0 && a.ring_k)
-            hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_ring_handoff<TIn>), dim3(a.B * a.Hkv), dim3(256), 0, stream, af);
     }
     return hipGetLastError();
 }

@@ -138,7 +138,7 @@ int prefill_impl(int parts, int mode, const void *q, const void *k, const void *
     const int s_per_query = mode == sfa::kQueryHead, running_mean = mode == sfa::kRunningMean;
     const int Hs = s_per_query ? Hq : Hkv;
 
-    sfa::PrefillArgs a;
+    sfa::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v;
     a.gamma = gamma; a.alpha = alpha;
     a.out = out; a.ring_k = ring_k; a.ring_v = ring_v; a.state = state; a.pos0 = pos0;

@@ -17,9 +17,14 @@ algorithmic bytes are one read of Q, K, V, one write of O and the ring
 hand-off.  The EWMA scan part (SFA_PREFILL_SCAN) runs just before it in every
 call and is part of the step time.
 
-Also reported in the same line: the 28-layer batched decode step (256
-sequences) and the 24-layer triple-channel enhancement, each with its own
-achieved HBM bandwidth, and the CPU fp64 oracle timed on this host.
+Also reported in the same line: the 0.5B-shaped prefill, the 28-layer batched
+decode step (256 sequences), the 24-layer triple-channel enhancement, the decode
+step fused with the enhancement and the far-field variants, each with its own
+achieved HBM bandwidth, and the CPU fp64 oracle timed on this host.  The
+shorter calls (the 0.5B-shaped prefill, the decode steps, the enhancement) are
+timed as HIP-graph replays of back-to-back calls over rotating input sets, with
+events only around the whole replay; the decode step and the enhancement also
+report the per-call HIP-event figure (`events_us_*`).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -227,6 +232,35 @@ def decode_bytes(L=28, Bd=256, Hq=28, Hkv=4, d=128, W=16):
     return L * Bd * per + Bd * 4
 
 
+def replay_ms(call, bufs, reps):
+    """Per-call time of `call` over the rotating input sets `bufs`: one call per
+    set, in order, captured once in a HIP graph; HIP events on the replay stream
+    bracket `reps` back-to-back replays, so no timing event sits between two
+    calls (each one idles the GPU for a few microseconds)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for d in bufs:  # first calls outside the capture
+            call(d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for d in bufs:
+            call(d)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        g.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * len(bufs))
+
+
 def run_decode(steps=40, warmup=5, sets=3):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -250,12 +284,16 @@ def run_decode(steps=40, warmup=5, sets=3):
         call(bufs[i % sets])
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    ms_ev = sum(a.elapsed_time(b) for a, b in ev) / steps
+    ms = replay_ms(lambda d: sfa.decode_step(d["q"], d["k_new"], d["v_new"], d["ring_k"], d["ring_v"], d["state"],
+                                             d["pos"], d["gamma"], d["alpha"], out=d["out"]),
+                   bufs, steps // sets + 1)
     ms_graph = decode_per_layer_graph(bufs, steps)
     byts = decode_bytes()
     return {"workload": "7B-shaped decode step, 28 layers x 256 sequences, 28/4 heads, d 128, bf16",
             "value": 28 * 256 * 28 / (ms * 1e-3), "unit": "tokens·heads/s (sequence, query head, layer)",
-            "us_per_step": ms * 1e3, "kernel": "k_decode_mfma",
+            "us_per_step": ms * 1e3, "timing": f"HIP-graph replays of {sets} rotating input sets",
+            "events_us_per_step": ms_ev * 1e3, "kernel": "k_decode_mfma",
             "per_layer_launches_graph_us_per_step": ms_graph * 1e3,
             "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
                          "unit": "GB/s", "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": byts}}
@@ -343,21 +381,9 @@ def run_variants(steps=10, warmup=2):
         dd["out"] = torch.empty((L, Bd, Hq, hd), dtype=torch.bfloat16, device=dev)
         sets.append(dd)
 
-    def call(dd):
-        sfa.decode_step(dd["q"], dd["k_new"], dd["v_new"], dd["ring_k"], dd["ring_v"], dd["state"],
-                        dd["pos"], dd["gamma"], dd["alpha"], out=dd["out"], stream=stream,
-                        gamma_per_query_head=True)
-
-    for i in range(3):
-        call(sets[i % 3])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * steps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        call(sets[i % 3])
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    ms = replay_ms(lambda dd: sfa.decode_step(dd["q"], dd["k_new"], dd["v_new"], dd["ring_k"], dd["ring_v"],
+                                              dd["state"], dd["pos"], dd["gamma"], dd["alpha"], out=dd["out"],
+                                              gamma_per_query_head=True), sets, 4 * steps // 3 + 1)
     byts = decode_bytes() + L * Bd * (Hq - Hkv) * hd * 4 * 2
     res["decode_qh"] = {"workload": "7B-shaped decode step, 28 layers x 256 sequences, γ and S per query head",
                         "us_per_step": ms * 1e3, "value": L * Bd * Hq / (ms * 1e-3),
@@ -402,20 +428,9 @@ def run_variants(steps=10, warmup=2):
         dd["out"] = torch.empty((L, Bd, Hq, hd), dtype=torch.bfloat16, device=dev)
         sets.append(dd)
 
-    def call_rm(dd):
-        sfa.decode_step(dd["q"], dd["k_new"], dd["v_new"], dd["ring_k"], dd["ring_v"], dd["state"],
-                        dd["pos"], dd["gamma"], dd["alpha"], out=dd["out"], stream=stream, running_mean=True)
-
-    for i in range(3):
-        call_rm(sets[i % 3])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * steps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        call_rm(sets[i % 3])
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    ms = replay_ms(lambda dd: sfa.decode_step(dd["q"], dd["k_new"], dd["v_new"], dd["ring_k"], dd["ring_v"],
+                                              dd["state"], dd["pos"], dd["gamma"], dd["alpha"], out=dd["out"],
+                                              running_mean=True), sets, 4 * steps // 3 + 1)
     byts = decode_bytes() + L * Bd * Hkv * hd * 4 * 2
     res["decode_rm"] = {"workload": "7B-shaped decode step, 28 layers x 256 sequences, running mean",
                         "us_per_step": ms * 1e3, "value": L * Bd * Hq / (ms * 1e-3),
@@ -533,9 +548,6 @@ def run_enhance(steps=20, warmup=3, sets=3):
         sfa.enhance_prepared(d["attn"], d["prepared"], d["ring"], d["field"], out=d["out"], workspace=ws,
                              stream=stream)
 
-    def call_per_call(d):
-        sfa.enhance(d["attn"], d["pool"], d["ring"], d["field"], out=d["out"], workspace=ws, stream=stream)
-
     def timed(fn):
         for i in range(warmup):
             fn(bufs[i % sets])
@@ -549,11 +561,17 @@ def run_enhance(steps=20, warmup=3, sets=3):
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / steps
 
-    ms = timed(call_prepared)
-    ms_pc = timed(call_per_call)
+    ms_ev = timed(call_prepared)
+    reps = steps // sets + 1
+    ms = replay_ms(lambda d: sfa.enhance_prepared(d["attn"], d["prepared"], d["ring"], d["field"], out=d["out"],
+                                                  workspace=ws), bufs, reps)
+    ms_pc = replay_ms(lambda d: sfa.enhance(d["attn"], d["pool"], d["ring"], d["field"], out=d["out"],
+                                            workspace=ws), bufs, reps)
     byts = enhance_bytes()
     return {"workload": "triple-channel enhancement, 24 layers x 4096 tokens, hidden 1024, 64 slots, bf16",
             "value": L * T / (ms * 1e-3), "unit": "tokens·layers/s", "us_per_call": ms * 1e3,
+            "timing": f"HIP-graph replays of {sets} rotating input sets",
+            "events_us_per_call": ms_ev * 1e3,
             "kernel": "sfa_enhance_prepared (3 launches: k_sem, k_field_carry, k_cols)",
             "per_call_prepare_us": ms_pc * 1e3,
             "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,

@@ -891,9 +891,20 @@ __device__ void call_tables_block(const EnhanceArgs &a, int bid) {
             a.alpha_tab[l] = al;
             // bf16 inputs: the semantic operands as single bf16 values where that
             // moves the layer's outputs by at most kSemSingleBound (see below)
-            const float *smax = reinterpret_cast<const float *>(pool_rec(a, a.n_pool_layers == 1 ? 0 : l)) + kSlots;
+            // (the 64 per-slot maxima as 16 loads issued together)
+            const float4 *smax = reinterpret_cast<const float4 *>(
+                reinterpret_cast<const float *>(pool_rec(a, a.n_pool_layers == 1 ? 0 : l)) + kSlots);
+            float4 mv[kSlots / 4];
+#pragma unroll
+            for (int k = 0; k < kSlots / 4; ++k) mv[k] = smax[k];
             float m = 0.f;
-            for (int s = 0; s < a.n_slots; ++s) m = fmaxf(m, smax[s]);
+#pragma unroll
+            for (int k = 0; k < kSlots / 4; ++k) {
+                if (4 * k + 0 < a.n_slots) m = fmaxf(m, mv[k].x);
+                if (4 * k + 1 < a.n_slots) m = fmaxf(m, mv[k].y);
+                if (4 * k + 2 < a.n_slots) m = fmaxf(m, mv[k].z);
+                if (4 * k + 3 < a.n_slots) m = fmaxf(m, mv[k].w);
+            }
             a.alpha_tab[a.L + l] = a.in_bf16 && fabsf(al) * kSemSingleErr * m <= kSemSingleBound ? 1.f : 0.f;
         }
         return;

@@ -49,7 +49,8 @@
  *    T == 0, L == 0) returns SFA_OK and enqueues nothing.
  *  - Thread safety: the library's global state is a per-device cache of how
  *    many decode workgroups the device holds at once (an atomic, written once
- *    per device with the value the runtime reports) and, for
+ *    per device with the value the runtime reports), a 1 KB device array that
+ *    the stores of skipped decode sequences go to (never read back) and, for
  *    sfa_prefill_noalloc only, a static scratch array per device with a cache
  *    of its address.  Concurrent calls are safe as long as they do not share
  *    output, state or workspace buffers, and no two sfa_prefill_noalloc calls

@@ -24,8 +24,9 @@
 //                  the tile, its field aggregate (EMA from zero).  Extra
 //                  workgroups copy the carried ring to the workspace.
 //   k_field_carry  field before each tile (exclusive scan), final field; extra
-//                  workgroups write the band/field operand table, α of each
-//                  layer and the new ring (the last min(R, T) attention rows).
+//                  workgroups write the band/field operand table, α and the
+//                  semantic-operand choice of each layer, and the new ring (the
+//                  last min(R, T) attention rows).
 //   k_cols         one workgroup per (layer, 64-token tile, 128 columns): the
 //                  tile staged column-major in LDS; ring mean, field and the
 //                  semantic sum as one MFMA contraction per 16-token group,
@@ -33,7 +34,9 @@
 // Precision: the fp32 pool, the softmax weights and the band/field
 // coefficients enter the MFMAs as bf16 hi + lo pairs (x = hi + lo to ~2^-17
 // relative); bf16 attention values are exact, fp32 attention values are split
-// the same way (and pass through the epilogue from LDS, unsplit).
+// the same way (and pass through the epilogue from LDS, unsplit).  With bf16
+// inputs, a layer whose error bound allows it (kSemSingleBound below) takes the
+// pool^T and weight operands of the semantic sum in k_cols as bf16 hi alone.
 #include <type_traits>
 
 #include "sfa_common.h"
@@ -56,7 +59,8 @@ constexpr int kTabEntries = kCoefEnt * 2 * 64;  // band/field operands (u32x4)
 // operands when α_l times that is at most kSemSingleBound.
 constexpr float kSemSingleErr = 0.5f * (0x1p-8f + 0x1p-18f);
 constexpr float kSemSingleBound = 1e-5f;
-// workgroups that write the band/field operand table and α of each layer
+// workgroups that write the band/field operand table, and α and the
+// semantic-operand choice of each layer
 __host__ __device__ inline int kCallTableBlocks(const EnhanceArgs &a) { return kTabEntries / 256 + (a.L + 255) / 256; }
 
 // sum over the 16 lanes of a DPP row (every lane of the row gets it)

@@ -544,7 +544,9 @@ __device__ __forceinline__ void store4<__bf16>(__bf16 *p, f32x4 v) {
     *reinterpret_cast<u32x2 *>(p) = w;
 }
 
-constexpr int kQSlots = 4;  // query heads whose Q operands are in flight together
+// query heads whose Q operands are in flight together: 4 at d = 128; at d = 64
+// the registers hold 8, so groups of up to 8 heads need no refills
+template <int D> constexpr int q_slots() { return D == 64 ? 8 : 4; }
 
 template <typename TOut>
 __device__ __forceinline__ void store8(TOut *p, const float *v);
@@ -623,10 +625,11 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
     // ---- (0) the first heads' queries go out before the K/V staging ----------
     // (B operands of the score MFMA: lane = token c16, 8 head-dim elements)
     // Qc[i] holds the head h with h % kQSlots == i; it is refilled with head
-    // h + kQSlots as soon as head h is done, so four heads are always in flight.
+    // h + kQSlots as soon as head h is done, so kQSlots heads are always in flight.
     // The loads are row-shaped: lane L reads the 16-byte chunk L % (D/8) of token
     // L / (D/8) (+ 64/(D/8) per load) of the block, whole rows per instruction;
     // an LDS tile turns them into MFMA operands.
+    constexpr int kQSlots = q_slots<D>();
     constexpr int CPT = D / 8, TPI = 64 / CPT, QLD = kBlk / TPI;
     const int rt = lane / CPT, rc = lane % CPT;
     const TIn *Qrow = reinterpret_cast<const TIn *>(a.q) + (((long)b * n + tb + rt) * a.Hq + (long)G * group) * D + 8 * rc;
@@ -1087,7 +1090,7 @@ __global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
 #pragma unroll
                 for (int st = 0; st < D / 32; ++st)
                     Qh[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&Ot[c16 * OS + 32 * st + 8 * q4]));
-                if (h + kQSlots < group) {  // refill the slot with head h + 4
+                if (h + kQSlots < group) {  // refill the slot with head h + kQSlots
 #pragma unroll
                     for (int j = 0; j < QLD; ++j)
                         if (tb + rt + TPI * j < n)

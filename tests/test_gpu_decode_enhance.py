@@ -77,6 +77,12 @@ def _stage_ref(d, a_rows, shared, layer0, nl):
 
 def _check(d, out_dtype, shared, layer0=0, n_layers=None):
     out, enh, c = _run(d, out_dtype, shared, layer0, n_layers)
+    _check_result(d, out, enh, c, out_dtype, shared, layer0, n_layers)
+
+
+def _check_result(d, out, enh, c, out_dtype, shared, layer0=0, n_layers=None):
+    """The GPU results (out, enhancement, updated state `c`) of inputs `d`
+    against the oracle."""
     nl = (layer0 + d["q"].shape[0]) if n_layers is None else n_layers
     ref = oracle.decode_step_enhance(d["q"], d["k_new"], d["v_new"], d["ring_k"], d["ring_v"], d["state"],
                                      d["pos"], d["gamma"], d["alpha"], d["pool"], d["e_ring"], d["field"],
@@ -204,3 +210,26 @@ def test_decode_step_enhance_steps_follow_a_gpu_prefill():
     for b in range(B):
         ref = oracle.enhance(rows[b][None], pool, shared_pool=True, ring_size=R, **kw)[0][0]
         check_output(got[b], ref[n:], True, f"enhanced outputs, sequence {b}")
+
+
+def test_decode_step_enhance_batch_256_sampled():
+    """The bench's 256-sequence fused step (28 layers, 28/4 heads, d 128, hidden
+    3,584, a 64-slot pool per layer, bf16 out).  Every (layer, sequence) is
+    independent, so the whole batch runs on the GPU and five sampled sequences
+    are checked against the oracle on those sequences alone, with the bars of
+    _check; every output of the batch must be finite."""
+    L, B, Hq, Hkv, hd, W, R, S = 28, 256, 28, 4, 128, 16, 16, 64
+    pos = [128 + (b * 997) % 8064 for b in range(B)]
+    log("decode + enhance, 256 sequences (sampled check)")
+    d = _inputs(L, B, Hq, Hkv, hd, W, R, S, seed=61, shared=False, pos=pos)
+    out, enh, c = _run(d, torch.bfloat16, False)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(enh).all()
+    sb = [0, 1, 77, 200, 255]
+    idx = torch.tensor(sb)
+    batch_dim = {"q": 1, "k_new": 1, "v_new": 1, "ring_k": 1, "ring_v": 1, "state": 1, "pos": 0, "e_ring": 1,
+                 "field": 1}
+    sub = {k: (v.index_select(batch_dim[k], idx).contiguous() if k in batch_dim else v) for k, v in d.items()}
+    csub = {k: (v.cpu().index_select(batch_dim[k], idx).contiguous() if k in batch_dim else v) for k, v in c.items()}
+    csub = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in csub.items()}
+    _check_result(sub, out.cpu()[:, idx].contiguous().cuda(), enh.cpu()[:, idx].contiguous().cuda(), csub,
+                  torch.bfloat16, False)

@@ -120,11 +120,29 @@ def _kw(d):
 
 
 def test_enhance_workload_24_layers():
-    """24 layers, hidden 1024, 4096 tokens, 64 slots, SFA_Config defaults."""
+    """24 layers, hidden 1024, 4096 tokens, 64 slots, SFA_Config defaults;
+    and the form bench.py times (sfa_enhance_prepared on the pool prepared
+    once, bf16 out) bit for bit equal to sfa_enhance on the same inputs."""
     d = inputs.workload(5)
     log("enhance triple-channel workload")
     ref = oracle.enhance(d["attn"], d["pool"], **_kw(d))
     _check(d["attn"], d["pool"], ref, **_kw(d))
+    L, T, H = d["attn"].shape
+    attn, pool = d["attn"].cuda(), d["pool"].cuda()
+    prep = sfa.enhance_prepare_pool(pool)
+    res = []
+    for fn in ("per-call", "prepared"):
+        ring = torch.zeros((L, 16, H), device="cuda")
+        field = torch.zeros((L, H), device="cuda")
+        kw = {k: v for k, v in _kw(d).items() if k != "ring_size"}
+        if fn == "per-call":
+            o, _ = sfa.enhance(attn, pool, ring, field, out_dtype=torch.bfloat16, **kw)
+        else:
+            o, _ = sfa.enhance_prepared(attn, prep, ring, field, out_dtype=torch.bfloat16, **kw)
+        torch.cuda.synchronize()
+        res.append((o, ring, field))
+    for x, y, name in zip(res[0], res[1], ("out", "ring", "field")):
+        assert torch.equal(x, y), name
 
 
 SMALL = [  # (L, T, H, n_slots, R, dtype)

@@ -142,3 +142,26 @@ def test_decode_negative_position_skips_the_sequence(hd):
     d = inputs.decode_inputs(L, B, Hq, Hkv, hd, seed=31 + hd)
     d["pos"] = torch.tensor([3, 40, 16, 15, 200, 7], dtype=torch.int32)
     _skip_case(d, 2, False)
+
+
+def test_decode_per_layer_launches_equal_one_launch_7b():
+    """The 7B-shaped step (28 layers x 256 sequences, 28/4 heads, d 128, bf16)
+    as 28 single-layer launches (the form bench.py replays per layer: one unit
+    per wave) equals the one launch over all layers bit for bit: out, both
+    rings and S.  (The one launch is checked against the oracle at this shape.)"""
+    log("decode 7B: 28 per-layer launches vs one launch")
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inputs.workload(3).items()}
+    L = d["q"].shape[0]
+    one = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    per = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    o1 = sfa.decode_step(one["q"], one["k_new"], one["v_new"], one["ring_k"], one["ring_v"], one["state"],
+                         one["pos"], one["gamma"], one["alpha"], out_dtype=torch.bfloat16)
+    o2 = torch.empty_like(o1)
+    for l in range(L):
+        sl = slice(l, l + 1)
+        sfa.decode_step(per["q"][sl], per["k_new"][sl], per["v_new"][sl], per["ring_k"][sl], per["ring_v"][sl],
+                        per["state"][sl], per["pos"], per["gamma"][sl], per["alpha"][sl], out=o2[sl])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "out"
+    for key in ("ring_k", "ring_v", "state"):
+        assert torch.equal(one[key], per[key]), key

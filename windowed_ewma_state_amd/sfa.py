@@ -2,8 +2,10 @@
 
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels behind include/sfa.h; PyTorch provides device memory and the current
-stream.  Names and argument meanings follow the C entry points
-(sfa_prefill, sfa_decode_step, sfa_enhance).
+stream.  Names and argument meanings follow the C entry points: prefill
+(sfa_prefill, sfa_prefill_part, sfa_prefill_qh, sfa_prefill_rm), prefill_noalloc,
+decode_step (sfa_decode_step, _qh, _rm), decode_step_enhance, enhance,
+enhance_prepare_pool and enhance_prepared, and the workspace and record sizes.
 """
 from __future__ import annotations
 

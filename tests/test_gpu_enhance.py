@@ -260,3 +260,66 @@ def test_enhance_prepared_pool_equals_per_call(shared):
     _check_elementwise(torch.cat([e for _, e in outs], 1), ref[1], dict(layer0=2, n_layers=5, **kw),
                        sem_single_extra(pool, dict(layer0=2, n_layers=5, **kw), L, shared, True))
     check_exact(g2[0], ref[2], "ring")
+
+
+# The one-pass form (bf16 inputs, hidden 256, 512, 768 or 1024): one workgroup
+# per (layer, 64-token tile) takes the field before its tile from the tiles
+# before it, up to 7 aggregates ahead of a published field-after, so these
+# cases span 1 .. 16 tiles, ragged tails, ring sizes below and above the tail,
+# layer counts that are not a multiple of 8 and both semantic operand forms
+# (α_base 0.7 keeps the pairs; 0.004 takes single operands in every layer).
+ONE_PASS = [  # (L, T, H, n_slots, R, alpha_base)
+    (1, 1, 256, 64, 16, 0.7), (3, 15, 512, 7, 16, 0.7), (9, 130, 256, 33, 4, 0.7),
+    (2, 1000, 768, 64, 16, 0.7), (1, 577, 1024, 64, 1, 0.7), (2, 64, 1024, 16, 16, 0.7),
+    (5, 520, 512, 64, 16, 0.004), (1, 1030, 256, 64, 13, 0.004),
+]
+
+
+@pytest.mark.parametrize("case", ONE_PASS, ids=lambda c: "L{}T{}H{}S{}R{}a{}".format(*c))
+def test_enhance_one_pass(case):
+    L, T, H, S, R, ab = case
+    log(f"enhance one-pass case {case}")
+    d = inputs.enhance_inputs(L, T, H, seed=3 * T + H + S, n_slots=S)
+    kw = dict(alpha_base=ab, cross_decay=0.9, ema_gamma=0.95, temperature=0.07, clip=0.5,
+              ring_size=R, t0=0)
+    ref = oracle.enhance(d["attn"], d["pool"], **kw)
+    _check(d["attn"], d["pool"], ref, **kw)
+
+
+@pytest.mark.parametrize("H", [256, 1024])
+def test_enhance_one_pass_continued_and_repeatable(H):
+    """A stream in three calls (t0 = 0, 300, 347; the middle call shorter than
+    the ring) against the oracle over the whole stream, with a non-zero carried
+    ring and field at the start; then the same three calls again, bit for bit."""
+    L, S, R = 3, 64, 16
+    d = inputs.enhance_inputs(L, 700, H, seed=H + 7, n_slots=S)
+    kw = dict(alpha_base=0.7, cross_decay=0.9, ema_gamma=0.97, temperature=0.07, clip=0.5,
+              ring_size=R, layer0=1, n_layers=6)
+    rng = np.random.default_rng(H)
+    # fp32 values, as the library holds them
+    ring0 = (rng.standard_normal((L, R, H)) * 0.5).astype(np.float32).astype(np.float64)
+    field0 = (rng.standard_normal((L, H)) * 0.5).astype(np.float32).astype(np.float64)
+    ref = oracle.enhance(d["attn"], d["pool"], ring0, field0, t0=11, **kw)
+    runs = []
+    for rep in range(2):
+        g_ring = torch.as_tensor(ring0, dtype=torch.float32).cuda().contiguous()
+        g_field = torch.as_tensor(field0, dtype=torch.float32).cuda().contiguous()
+        pool = d["pool"].cuda()
+        outs, enhs = [], []
+        for a0, a1 in ((0, 300), (300, 347), (347, 700)):
+            a = d["attn"][:, a0:a1].contiguous().cuda()
+            e = torch.empty(a.shape, dtype=torch.float32, device="cuda")
+            o, _ = sfa.enhance(a, pool, g_ring, g_field, out_dtype=torch.bfloat16, enhancement=e,
+                               t0=11 + a0, **{k: v for k, v in kw.items() if k != "ring_size"})
+            outs.append(o)
+            enhs.append(e)
+        torch.cuda.synchronize()
+        runs.append((torch.cat(outs, 1), torch.cat(enhs, 1), g_ring, g_field))
+    out, enh, g_ring, g_field = runs[0]
+    check_output(out, ref[0], True, "out")
+    assert rel_l2(enh, ref[1]) <= 2e-4
+    _check_elementwise(enh, ref[1], kw)
+    check_exact(g_ring, ref[2], "ring")
+    assert rel_l2(g_field, ref[3]) <= 1e-5
+    for x, y, name in zip(runs[0], runs[1], ("out", "enhancement", "ring", "field")):
+        assert torch.equal(x, y), f"repeat differs: {name}"

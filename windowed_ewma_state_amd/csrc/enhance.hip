@@ -272,21 +272,8 @@ __global__ __launch_bounds__(256) void k_field_carry(EnhanceArgs a) {
 // through the softmax over the slots and writes 0.5·w as the bf16 hi/lo B
 // operands of the semantic sum.
 // ---------------------------------------------------------------------------
-// eight attention values (raw 16-byte words) -> bf16 hi (+ lo for fp32) and Σa²
-template <typename TIn>
-__device__ __forceinline__ void split_a8(const u32x4 *w, bf16x8 &hi, bf16x8 &lo, float &sq);
-template <>
-__device__ __forceinline__ void split_a8<__bf16>(const u32x4 *w, bf16x8 &hi, bf16x8 &lo, float &sq) {
-    hi = __builtin_bit_cast(bf16x8, w[0]);
-    lo = bf16x8{};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float v = (float)hi[e];
-        sq = fmaf(v, v, sq);
-    }
-}
-template <>
-__device__ __forceinline__ void split_a8<float>(const u32x4 *w, bf16x8 &hi, bf16x8 &lo, float &sq) {
+// eight fp32 attention values (two raw 16-byte words) -> bf16 hi + lo and Σa²
+__device__ __forceinline__ void split_a8(const u32x4 *w, bf16x8 &hi, bf16x8 &lo, float &sq) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float v = __uint_as_float(w[e >> 2][e & 3]);
@@ -357,13 +344,13 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) C[j][tg] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // rows past the end read the tile's first row: their scores and weights
+    // only reach outputs that are never stored, and their field weight is 0
     const TIn *arow[4];
-    bool tok_ok[4];
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
         const int t = tb + 16 * tg + c16;
-        tok_ok[tg] = t < T;
-        arow[tg] = Ag + (long)(tok_ok[tg] ? t : tb) * H + 8 * q4;
+        arow[tg] = Ag + (long)(t < T ? t : tb) * H + 8 * q4;
     }
     // k-step operands: attention values of the four token groups and the pool
     // tiles
@@ -391,8 +378,17 @@ __global__ __launch_bounds__(256, 2) void k_sem(EnhanceArgs a) {
         bf16x8 bh[4], bl[4];
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-            split_a8<TIn>(o.a[tg], bh[tg], bl[tg], sq[tg]);
-            if (!tok_ok[tg]) bh[tg] = bl[tg] = bf16x8{};
+            if constexpr (kPrecise) {
+                split_a8(o.a[tg], bh[tg], bl[tg], sq[tg]);
+            } else {
+                bh[tg] = __builtin_bit_cast(bf16x8, o.a[tg][0]);
+                bl[tg] = bf16x8{};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = (float)bh[tg][e];
+                    sq[tg] = fmaf(v, v, sq[tg]);
+                }
+            }
         }
         if (fuse_agg) {
             // Σ_t (1-γ)γ^(len-1-t)·a[t][x] over the lane's 4 tokens, then over

@@ -568,8 +568,13 @@ __device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float *v) {
 // RM: the running mean of the keys that have left the window is the EWMA
 // input; the wave starts from the tile's carried (S, C) and the block
 // aggregates of its earlier blocks, then scans C += k, S = γS + (1-γ)·C/m.
+// Two workgroups per CU, except fp32 inputs at d = 128: their fp32 K rows and
+// split V^T staging take 119 KB of LDS, so one workgroup per CU is all the
+// LDS allows and the register budget follows that.
+template <typename TIn, int D>
+constexpr int attn_wg_per_cu() { return std::is_same<TIn, float>::value && D == 128 ? 1 : 2; }
 template <typename TIn, typename TOut, int D, int MODE, bool FUSED = false, bool FOLD = false>
-__global__ __launch_bounds__(256, 2) void k_window_attn(PrefillArgs a) {
+__global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn(PrefillArgs a) {
     constexpr bool QH = MODE == kQueryHead, RM = MODE == kRunningMean;
     constexpr bool kBf16 = std::is_same<TIn, __bf16>::value;
     constexpr int EPL = D / kWave;

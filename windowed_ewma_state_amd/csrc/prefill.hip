@@ -170,10 +170,17 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
                         A[cc][e] = gm * A[cc][e] + (1.f - gm) * (Cs[cc][e] * inv_m);
                     }
                 } else {
+                    // A/(1-γ) as one FMA per step; the factor is applied once below
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) A[cc][e] = gm * A[cc][e] + (1.f - gm) * v[e];
+                    for (int e = 0; e < EPC; ++e) A[cc][e] = fmaf(gm, A[cc][e], v[e]);
                 }
             }
+        }
+        if constexpr (!RM) {
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) A[cc][e] *= 1.f - gm;
         }
     }
     // 16-token block aggregates, then the tile aggregate: blocks combined in
@@ -191,8 +198,9 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
         }
     }
     // (S per KV head with bf16 inputs, the attention kernel forms the block
-    // aggregates from its own scan and reads only the tile carries)
-    constexpr bool kWrite16 = RM || QH || sizeof(TIn) != 2;
+    // aggregates from its own scan and reads only the tile carries; with γ per
+    // query head the tile composition below writes the running partials)
+    constexpr bool kWrite16 = RM || (!QH && sizeof(TIn) != 2);
     if (lane_ok && kWrite16) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
@@ -228,6 +236,11 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
         float T = 0.f, TC = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
+            // QH: slot w-1 holds P(w), the EWMA from zero over blocks 0 .. w-1
+            // (what block w starts from before the tile's carry is added)
+            if constexpr (QH) {
+                if (w > 0) a.agg16[(trec * 4 + w - 1) * D + e] = T;
+            }
             if constexpr (RM) {
                 T = decay[wave][w] * T + beta[wave][w] * TC + blkv[wave][w][e];
                 TC += blkc[wave][w][e];
@@ -661,13 +674,21 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
         const float *C = a.carry + tbase * D + e0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) Cx[e] = C[e];
-        // (all three blocks are loaded unconditionally, in bounds for every
-        // wave; only w < wave are used)
+        if constexpr (QH) {
+            // the partial P(wave) of this wave's block start (wave 0 loads P(1)
+            // and ignores it: one unconditional load keeps the waits exact)
+            const float *A = a.agg16 + (tbase * 4 + max(wave - 1, 0)) * D + e0;
 #pragma unroll
-        for (int w = 0; w < 3; ++w) {
-            const float *A = a.agg16 + (tbase * 4 + w) * D + e0;
+            for (int e = 0; e < EPL; ++e) Ax[0][e] = A[e];
+        } else {
+            // (all three blocks are loaded unconditionally, in bounds for every
+            // wave; only w < wave are used)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) Ax[w][e] = A[e];
+            for (int w = 0; w < 3; ++w) {
+                const float *A = a.agg16 + (tbase * 4 + w) * D + e0;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) Ax[w][e] = A[e];
+            }
         }
     };
     // QH: chain of query head h of this group
@@ -826,15 +847,23 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
     // ---- (2) S just before this wave's 16-token block (KV heads) ------------
     // S_{block start} = carry through the wave's earlier blocks of the tile
     auto block_start = [&](float g, const float *Cx, float (*Ax)[EPL], float *Sx) {
+        if constexpr (QH) {
+            // S = (decay over blocks 0 .. wave-1)·C + P(wave)
+            const int s0 = t0, len = min(kBlk * wave, n - s0);
+            const float gw = powi(g, evict_steps(p0, s0, max(len, 0), W));
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) Sx[e] = Cx[e];
+            for (int e = 0; e < EPL; ++e) Sx[e] = wave > 0 ? gw * Cx[e] + Ax[0][e] : Cx[e];
+        } else {
 #pragma unroll
-        for (int w = 0; w < 3; ++w) {
-            if (w < wave) {
-                const int s0 = t0 + kBlk * w;
-                const float gl = powi(g, evict_steps(p0, s0, min(kBlk, n - s0), W));
+            for (int e = 0; e < EPL; ++e) Sx[e] = Cx[e];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) Sx[e] = gl * Sx[e] + Ax[w][e];
+            for (int w = 0; w < 3; ++w) {
+                if (w < wave) {
+                    const int s0 = t0 + kBlk * w;
+                    const float gl = powi(g, evict_steps(p0, s0, min(kBlk, n - s0), W));
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) Sx[e] = gl * Sx[e] + Ax[w][e];
+                }
             }
         }
     };

@@ -163,25 +163,23 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(raw[j][cc][i]);
                 }
+                // A/(1-γ), one FMA per step; the factor is applied once below
                 if constexpr (RM) {
 #pragma unroll
                     for (int e = 0; e < EPC; ++e) {
                         Cs[cc][e] += v[e];
-                        A[cc][e] = gm * A[cc][e] + (1.f - gm) * (Cs[cc][e] * inv_m);
+                        A[cc][e] = fmaf(gm, A[cc][e], Cs[cc][e] * inv_m);
                     }
                 } else {
-                    // A/(1-γ) as one FMA per step; the factor is applied once below
 #pragma unroll
                     for (int e = 0; e < EPC; ++e) A[cc][e] = fmaf(gm, A[cc][e], v[e]);
                 }
             }
         }
-        if constexpr (!RM) {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc)
+        for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) A[cc][e] *= 1.f - gm;
-        }
+            for (int e = 0; e < EPC; ++e) A[cc][e] *= 1.f - gm;
     }
     // 16-token block aggregates, then the tile aggregate: blocks combined in
     // order through LDS, T = ((A0·g1 + A1)·g2 + A2)·g3 + A3 with g_w the decay

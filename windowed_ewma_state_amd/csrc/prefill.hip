@@ -8,10 +8,14 @@
 // leaving the window) and the fusion equation; section 2.2 (O(k·n·d) time).
 //
 // Three launches per call:
-//   k_ewma_agg    one workgroup per (b, KV head, 64-token tile): local EWMA
-//                 aggregate of each 16-token block and of the tile (scan from 0).
-//   k_ewma_carry  one workgroup per (b, KV head): exclusive scan of the tile
-//                 aggregates -> S just before every tile; writes the final S.
+//   k_ewma_agg    one wave per (b, KV head, 64-token tile): the tile's local
+//                 EWMA aggregate (scan from 0) and, where the attention kernel
+//                 reads them, its 16-token blocks' (fp32 inputs; with the
+//                 running mean, their key sums; with γ per query head, as
+//                 block-start partials of every query head's chain).
+//   k_ewma_carry  one workgroup per (scan chain, 16 head-dim columns):
+//                 exclusive scan of the tile aggregates -> S just before every
+//                 tile; writes the final S.
 //   k_window_attn one workgroup per (b, KV head, tile), XCD-aware order:
 //                 stages K rows [t0-16, t0+64) row-major and V transposed in
 //                 LDS, shared by all query heads of the GQA group; each wave
@@ -69,9 +73,11 @@ __device__ __forceinline__ void load_epl(const T *p, float *x) {
 
 // ---------------------------------------------------------------------------
 // k_ewma_agg: local aggregates A (EWMA from zero) of 16-token blocks and tiles.
-// One wave per 64-token tile of one (b, KV head) chain (four chains per workgroup).  Lane (w, c) owns the
-// 16-byte chunk c of the head dimension for block w of the tile, so every load
-// is a 16-byte vector and a block's 16 rows are in flight together.
+// One wave per 64-token tile of one (b, KV head) chain (four chains per
+// workgroup).  Lane (w, c) owns the 16-byte chunk c of the head dimension for
+// block w of the tile, so every load is a 16-byte vector and a block's 16 rows
+// are in flight together.  A block's scan carries A/(1-γ), one FMA per evicted
+// key and element, and applies (1-γ) once at its end.
 //
 // RM (running mean of the keys that have left the window): a segment maps the
 // incoming (S, C) to g·S + β·C + s and C + c, with g = γ^(evicting steps), c

@@ -6,8 +6,10 @@ several tiles (and, for the 64K layer, 16), in the three modes the library
 exports: S per KV head (sfa_prefill), γ and S per query head (sfa_prefill_qh)
 and the running mean of the keys that have left the window (sfa_prefill_rm).
 They cover a full 65,536-token 7B-shaped layer in the launch configuration the
-bench times (bf16 in, bf16 out), ragged lengths, a second chunk continuing a
-first one, and continuations from per-sequence positions beyond 64 tiles.
+bench times (bf16 in, bf16 out), ragged lengths (one past 65,536 tokens, where
+a part folds more tiles than the scan keeps in registers), a second chunk
+continuing a first one, and continuations from per-sequence positions beyond
+64 tiles.
 Tolerances are those of tests/parity.py.
 """
 import numpy as np
@@ -84,6 +86,7 @@ RAGGED = [  # (B, n, Hq, Hkv, hd, W, dtype)
     (2, 4096 + 64 * 9 + 1, 7, 1, 128, 5, torch.bfloat16),
     (1, 4700, 4, 2, 64, 16, torch.float32),
     (1, 6000 + 3, 8, 2, 128, 16, torch.float32),
+    (1, 65536 + 4096 + 37, 2, 1, 64, 16, torch.bfloat16),  # 1,089 tiles: 18 per carry part
 ]
 
 

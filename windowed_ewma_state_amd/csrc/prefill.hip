@@ -279,11 +279,12 @@ __device__ __forceinline__ int evict_steps(int p0, int s0, int len, int W) {
 // ---------------------------------------------------------------------------
 // k_ewma_carry: S before each tile (exclusive scan over tiles) and final S.
 // One workgroup per (b, KV head, 16 head-dim elements); 64 parts of the tile
-// range are scanned in parallel (all loads of a part issued together), the
-// part aggregates are combined by a log-step scan through LDS, and each part
-// is rescanned from its carry-in.
+// range are scanned in parallel (up to kCarryRegs tiles per part: every load
+// of the part issued at once and kept in registers for the rescan), the part
+// aggregates are combined by one wave per column (a shuffle scan over the 64
+// parts, between two barriers), and each part is rescanned from its carry-in.
 // ---------------------------------------------------------------------------
-constexpr int kCarryParts = 64, kCarryCols = 16;
+constexpr int kCarryParts = 64, kCarryCols = 16, kCarryRegs = 16;
 
 // RM: the same scan over the affine maps (g, β, s, c) of the tiles, carrying
 // (S, C); parts compose as (G, B, X, Cx) then (g, β, s, c) ->
@@ -291,6 +292,7 @@ constexpr int kCarryParts = 64, kCarryCols = 16;
 // and the final mean C/m.
 template <bool RM>
 __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
+    static_assert(kCarryParts == kWave && kCarryCols * kCarryParts == 1024, "one wave per column, one lane per part");
     __shared__ float partX[kCarryParts][kCarryCols];
     __shared__ float partC[RM ? kCarryParts : 1][kCarryCols];
     __shared__ float partG[kCarryParts], partB[kCarryParts];
@@ -299,6 +301,7 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
     const int bg = blockIdx.x / cblocks;
     const int e = (blockIdx.x % cblocks) * kCarryCols + threadIdx.x % kCarryCols;
     const int part = threadIdx.x / kCarryCols;
+    const int col = threadIdx.x % kCarryCols;
     const int b = bg / a.Hs, hs = bg % a.Hs;
     const int n = a.n, W = a.W, nt = a.ntiles;
     const int p0 = a.pos0 ? max(0, a.pos0[b]) : 0;
@@ -319,50 +322,89 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
         const int st = evict_steps(p0, i * kTile, len, W);
         return st == kTile ? g64 : powi(gm, st);
     };
-    float X = 0.f, Gam = 1.f, Bc = 0.f, Cx = 0.f;
-#pragma unroll 8
-    for (int i = i0; i < i1; ++i) {
-        const float gl = decay_of(i);
-        if constexpr (RM) {
-            const float be = Bt[i];
-            X = gl * X + be * Cx + A[(long)i * D];
-            Cx += Cs[(long)i * D];
-            Bc = gl * Bc + be;
-        } else {
-            X = gl * X + A[(long)i * D];
-        }
-        Gam *= gl;
-    }
-    // inclusive scan of the part aggregates over parts, log2(parts) steps:
-    // (X_a, Γ_a) then (X_b, Γ_b) combine to (Γ_b·X_a + X_b, Γ_a·Γ_b)
-    // (RM: X = Γ_b·X_a + B_b·Cx_a + X_b, Cx = Cx_a + Cx_b, B = Γ_b·B_a + B_b)
-    const int col = threadIdx.x % kCarryCols;
+    // the part's tiles in registers when it has at most kCarryRegs of them
+    // (tiles past the part read its first tile and are never used)
+    const bool regs = per <= kCarryRegs;
+    float Ar[kCarryRegs], Cr[RM ? kCarryRegs : 1], Br[RM ? kCarryRegs : 1];
+    if (regs) {
 #pragma unroll
-    for (int off = 1; off < kCarryParts; off <<= 1) {
-        partX[part][col] = X;
-        if constexpr (RM) partC[part][col] = Cx;
-        if (col == 0) {
-            partG[part] = Gam;
-            partB[part] = Bc;
-        }
-        __syncthreads();
-        if (part >= off) {
+        for (int j = 0; j < kCarryRegs; ++j) {
+            const int i = i0 + j < i1 ? i0 + j : min(i0, nt - 1);
+            Ar[j] = A[(long)i * D];
             if constexpr (RM) {
-                X = Gam * partX[part - off][col] + Bc * partC[part - off][col] + X;
-                Cx = partC[part - off][col] + Cx;
-                Bc = Gam * partB[part - off] + Bc;
-            } else {
-                X = Gam * partX[part - off][col] + X;
+                Cr[j] = Cs[(long)i * D];
+                Br[j] = Bt[i];
             }
-            Gam = partG[part - off] * Gam;
         }
-        __syncthreads();
     }
+    float X = 0.f, Gam = 1.f, Bc = 0.f, Cx = 0.f;
+    if (regs) {
+#pragma unroll
+        for (int j = 0; j < kCarryRegs; ++j) {
+            if (i0 + j < i1) {
+                const float gl = decay_of(i0 + j);
+                if constexpr (RM) {
+                    X = gl * X + Br[j] * Cx + Ar[j];
+                    Cx += Cr[j];
+                    Bc = gl * Bc + Br[j];
+                } else {
+                    X = gl * X + Ar[j];
+                }
+                Gam *= gl;
+            }
+        }
+    } else {
+#pragma unroll 8
+        for (int i = i0; i < i1; ++i) {
+            const float gl = decay_of(i);
+            if constexpr (RM) {
+                const float be = Bt[i];
+                X = gl * X + be * Cx + A[(long)i * D];
+                Cx += Cs[(long)i * D];
+                Bc = gl * Bc + be;
+            } else {
+                X = gl * X + A[(long)i * D];
+            }
+            Gam *= gl;
+        }
+    }
+    // inclusive scan of the part aggregates over parts: wave w takes column
+    // w, lane = part, log2(parts) shuffle steps with the combine
+    // (X_a, Γ_a) then (X_b, Γ_b) -> (Γ_b·X_a + X_b, Γ_a·Γ_b)
+    // (RM: X = Γ_b·X_a + B_b·Cx_a + X_b, Cx = Cx_a + Cx_b, B = Γ_b·B_a + B_b)
     partX[part][col] = X;
     if constexpr (RM) partC[part][col] = Cx;
     if (col == 0) {
         partG[part] = Gam;
         partB[part] = Bc;
+    }
+    __syncthreads();
+    {
+        const int w = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+        float x = partX[ln][w], g = partG[ln];
+        float c = RM ? partC[ln][w] : 0.f, bb = RM ? partB[ln] : 0.f;
+#pragma unroll
+        for (int off = 1; off < kCarryParts; off <<= 1) {
+            const float px = __shfl_up(x, off), pg = __shfl_up(g, off);
+            const float pc = RM ? __shfl_up(c, off) : 0.f, pb = RM ? __shfl_up(bb, off) : 0.f;
+            if (ln >= off) {
+                if constexpr (RM) {
+                    x = g * px + bb * pc + x;
+                    c = pc + c;
+                    bb = g * pb + bb;
+                } else {
+                    x = g * px + x;
+                }
+                g = pg * g;
+            }
+        }
+        __syncthreads();  // every wave has read the part aggregates
+        partX[ln][w] = x;
+        if constexpr (RM) partC[ln][w] = c;
+        if (w == 0) {
+            partG[ln] = g;
+            partB[ln] = bb;
+        }
     }
     __syncthreads();
     // carry into this part: (S_init, C_init) through all earlier parts
@@ -377,15 +419,32 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
     float *Cout = a.carry + (long)bg * nt * D + e;
     float *Kout = RM ? a.ccarry + (long)bg * nt * D + e : nullptr;
     X = C;
+    if (regs) {
+#pragma unroll
+        for (int j = 0; j < kCarryRegs; ++j) {
+            if (i0 + j < i1) {
+                const int i = i0 + j;
+                Cout[(long)i * D] = X;
+                if constexpr (RM) {
+                    Kout[(long)i * D] = K;
+                    X = decay_of(i) * X + Br[j] * K + Ar[j];
+                    K += Cr[j];
+                } else {
+                    X = decay_of(i) * X + Ar[j];
+                }
+            }
+        }
+    } else {
 #pragma unroll 8
-    for (int i = i0; i < i1; ++i) {
-        Cout[(long)i * D] = X;
-        if constexpr (RM) {
-            Kout[(long)i * D] = K;
-            X = decay_of(i) * X + Bt[i] * K + A[(long)i * D];
-            K += Cs[(long)i * D];
-        } else {
-            X = decay_of(i) * X + A[(long)i * D];
+        for (int i = i0; i < i1; ++i) {
+            Cout[(long)i * D] = X;
+            if constexpr (RM) {
+                Kout[(long)i * D] = K;
+                X = decay_of(i) * X + Bt[i] * K + A[(long)i * D];
+                K += Cs[(long)i * D];
+            } else {
+                X = decay_of(i) * X + A[(long)i * D];
+            }
         }
     }
     if (part == kCarryParts - 1 && a.state) {

@@ -317,11 +317,12 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
     const float *A = a.agg64 + (long)bg * nt * D + e;
     const float *Cs = RM ? a.csum64 + (long)bg * nt * D + e : nullptr;
     const float *Bt = RM ? a.beta64 + (long)bg * nt : nullptr;
-    auto decay_of = [&](int i) {
-        const int len = min(kTile, n - i * kTile);
-        const int st = evict_steps(p0, i * kTile, len, W);
-        return st == kTile ? g64 : powi(gm, st);
-    };
+    // γ^(evicting steps of tile i): every tile but the first (which may start
+    // inside the first window, W <= 16 < 64) and the last (which may be
+    // short) evicts 64 keys
+    const float g_first = powi(gm, evict_steps(p0, 0, min(kTile, n), W));
+    const float g_last = powi(gm, evict_steps(p0, (nt - 1) * kTile, n - (nt - 1) * kTile, W));
+    auto decay_of = [&](int i) { return i == 0 ? g_first : i == nt - 1 ? g_last : g64; };
     // the part's tiles in registers when it has at most kCarryRegs of them
     // (tiles past the part read its first tile and are never used)
     const bool regs = per <= kCarryRegs;
@@ -339,19 +340,20 @@ __global__ __launch_bounds__(1024) void k_ewma_carry(PrefillArgs a) {
     }
     float X = 0.f, Gam = 1.f, Bc = 0.f, Cx = 0.f;
     if (regs) {
+        // tiles past the part fold as the identity (decay 1, zero terms)
 #pragma unroll
         for (int j = 0; j < kCarryRegs; ++j) {
-            if (i0 + j < i1) {
-                const float gl = decay_of(i0 + j);
-                if constexpr (RM) {
-                    X = gl * X + Br[j] * Cx + Ar[j];
-                    Cx += Cr[j];
-                    Bc = gl * Bc + Br[j];
-                } else {
-                    X = gl * X + Ar[j];
-                }
-                Gam *= gl;
+            const bool in = i0 + j < i1;
+            const float gl = in ? decay_of(i0 + j) : 1.f, av = in ? Ar[j] : 0.f;
+            if constexpr (RM) {
+                const float be = in ? Br[j] : 0.f;
+                X = gl * X + be * Cx + av;
+                Cx += in ? Cr[j] : 0.f;
+                Bc = gl * Bc + be;
+            } else {
+                X = gl * X + av;
             }
+            Gam *= gl;
         }
     } else {
 #pragma unroll 8

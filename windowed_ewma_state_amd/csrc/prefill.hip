@@ -201,10 +201,11 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
             if (p >= W) bw = gm * bw + (1.f - gm) / (float)(p - W + 1);
         }
     }
-    // (S per KV head with bf16 inputs, the attention kernel forms the block
-    // aggregates from its own scan and reads only the tile carries; with γ per
-    // query head the tile composition below writes the running partials)
-    constexpr bool kWrite16 = RM || (!QH && sizeof(TIn) != 2);
+    // (with bf16 inputs and S per KV head, plain or with the running mean, the
+    // attention kernel forms the block maps from its own scan and reads only
+    // the tile carries; with γ per query head the tile composition below
+    // writes the running partials)
+    constexpr bool kWrite16 = !QH && sizeof(TIn) != 2;
     if (lane_ok && kWrite16) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
@@ -467,6 +468,29 @@ template <int SH>
 __device__ __forceinline__ float row_shr(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + SH, 0xf, 0xf, true));
 }
+// one step of a log-step prefix sum over the 16 lanes of a DPP row
+template <int SH, int NK>
+__device__ __forceinline__ void row_sum_step(f32x4 (*V)[2]) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) V[k][half][i] += row_shr<SH>(V[k][half][i]);
+}
+// the same scan as row_scan_step carrying a second, scalar V (B = A·B + β)
+template <int SH, int NK>
+__device__ __forceinline__ void row_scan_step2(f32x4 (*V)[2], float &B, float &A, int c16) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) V[k][half][i] = fmaf(A, row_shr<SH>(V[k][half][i]), V[k][half][i]);
+    B = fmaf(A, row_shr<SH>(B), B);
+    const float Ap = row_shr<SH>(A);
+    A = c16 >= SH ? A * Ap : A;
+}
 template <int SH, int NK>
 __device__ __forceinline__ void row_scan_step(f32x4 (*V)[2], float &A, int c16) {
 #pragma unroll
@@ -667,13 +691,19 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
     // S per KV head with bf16 inputs stays in registers (epilogue layout, a row
     // scan over the wave's 16 tokens); the LDS slot then only carries S at the
     // block start.  The other modes keep each token's S row in LDS.
-    constexpr bool kRegS = !QH && !RM && kBf16;
-    static_assert(!(FUSED || FOLD) || kRegS, "the single-pass and folded forms exist for S per KV head with bf16 inputs");
+    constexpr bool kRegS = !QH && kBf16;
+    static_assert(!(FUSED || FOLD) || (kRegS && !RM), "the single-pass and folded forms exist for S per KV head with bf16 inputs");
     static_assert(!(FUSED && FOLD), "one carry form at a time");
     __shared__ __attribute__((aligned(16))) float Sb[4][kRegS ? D : kBlk * SS];
     // kRegS: each wave's block aggregate (the EWMA of its 16 tokens from zero);
     // single pass: the waves' partial folds of the earlier tiles' aggregates
     __shared__ __attribute__((aligned(16))) float BlkAgg[kRegS ? 4 : 1][kRegS ? D : 1];
+    // kRegS with the running mean: each wave's block key sum, its map's decay
+    // and β, and the key sum C at its block start
+    constexpr bool kRegC = kRegS && RM;
+    __shared__ __attribute__((aligned(16))) float BlkC[kRegC ? 4 : 1][kRegC ? D : 1];
+    __shared__ __attribute__((aligned(16))) float Kb[kRegC ? 4 : 1][kRegC ? D : 1];
+    __shared__ float BlkG[4], BlkB[4];
     __shared__ __attribute__((aligned(16))) float FoldX[FUSED || FOLD ? 4 : 1][FUSED || FOLD ? D : 1];
     __shared__ float FoldG[4];
 
@@ -787,16 +817,19 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
     } else {
         carry_loads(chain0, Cin, Ain);
     }
-    // RM: the key sum carried into the tile and the earlier blocks' key sums
-    float Kin[RM ? EPL : 1], Kblk[RM ? 3 : 1][RM ? EPL : 1];
+    // RM: the key sum carried into the tile and (S rows in LDS) the earlier
+    // blocks' key sums
+    float Kin[RM ? EPL : 1], Kblk[RM && !kRegS ? 3 : 1][RM && !kRegS ? EPL : 1];
     if constexpr (RM) {
         const long tbase = chain0 * a.ntiles + tile;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) Kin[e] = a.ccarry[tbase * D + e0 + e];
+        if constexpr (!kRegS) {
 #pragma unroll
-        for (int w = 0; w < 3; ++w)
+            for (int w = 0; w < 3; ++w)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) Kblk[w][e] = a.csum16[(tbase * 4 + w) * D + e0 + e];
+                for (int e = 0; e < EPL; ++e) Kblk[w][e] = a.csum16[(tbase * 4 + w) * D + e0 + e];
+        }
     }
 
     // ---- (1) stage K rows (row-major) and V (transposed) ---------------------
@@ -938,6 +971,7 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
     // staging area is reused in the head loop)
     float kev[QH ? kBlk : 1][EPL];
     float Ac = 1.f;  // kRegS: decay from the block start to the lane's token
+    float Bq = 0.f;  // kRegC: weight of the block-start key sum in the lane's S
     if constexpr (kRegS) {
         __syncthreads();
         // ---- (3) EWMA through the block from zero, then the block aggregate ----
@@ -952,24 +986,62 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
         const float w1 = ev ? 1.f - gm : 0.f;
         // token t - W sits in staged row (t - W) - (t0 - 16)
         const TIn *kr = &Klds[(kBlk * wave + c16 + kMaxWindow - W) * KS + 8 * q4];
+        f32x4 Kreg[kRegC ? D / 32 : 1][2];
 #pragma unroll
         for (int k = 0; k < D / 32; ++k) {
             const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(kr + 32 * k);
 #pragma unroll
             for (int half = 0; half < 2; ++half)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Sreg[k][half][i] = w1 * (float)kk[4 * half + i];
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (kRegC)
+                        Kreg[k][half][i] = ev ? (float)kk[4 * half + i] : 0.f;
+                    else
+                        Sreg[k][half][i] = w1 * (float)kk[4 * half + i];
+                }
         }
-        row_scan_step<1, D / 32>(Sreg, Ac, c16);
-        row_scan_step<2, D / 32>(Sreg, Ac, c16);
-        row_scan_step<4, D / 32>(Sreg, Ac, c16);
-        row_scan_step<8, D / 32>(Sreg, Ac, c16);
-        if (c16 == kBlk - 1) {
+        if constexpr (kRegC) {
+            // running mean: per evicting token C += k and S = γ·S + β_t·C with
+            // β_t = (1-γ)/m_t.  From the block start (S0, C0), C_t = C0 + K_t
+            // (K_t the block's prefix sum of evicted keys) and
+            // S_t = Γ_t·S0 + B_t·C0 + V_t, where V_t = γ_t·V_{t-1} + β_t·K_t
+            // and B_t = γ_t·B_{t-1} + β_t: a prefix sum, then the scan of
+            // (γ_t, β_t·K_t) carrying B beside V.
+            const float bt = ev ? (1.f - gm) / (float)(p0 + t - W + 1) : 0.f;
+            row_sum_step<1, D / 32>(Kreg);
+            row_sum_step<2, D / 32>(Kreg);
+            row_sum_step<4, D / 32>(Kreg);
+            row_sum_step<8, D / 32>(Kreg);
 #pragma unroll
             for (int k = 0; k < D / 32; ++k)
 #pragma unroll
                 for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Sreg[k][half][i] = bt * Kreg[k][half][i];
+            Bq = bt;
+            row_scan_step2<1, D / 32>(Sreg, Bq, Ac, c16);
+            row_scan_step2<2, D / 32>(Sreg, Bq, Ac, c16);
+            row_scan_step2<4, D / 32>(Sreg, Bq, Ac, c16);
+            row_scan_step2<8, D / 32>(Sreg, Bq, Ac, c16);
+        } else {
+            row_scan_step<1, D / 32>(Sreg, Ac, c16);
+            row_scan_step<2, D / 32>(Sreg, Ac, c16);
+            row_scan_step<4, D / 32>(Sreg, Ac, c16);
+            row_scan_step<8, D / 32>(Sreg, Ac, c16);
+        }
+        if (c16 == kBlk - 1) {
+#pragma unroll
+            for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
                     *reinterpret_cast<f32x4 *>(&BlkAgg[wave][32 * k + 8 * q4 + 4 * half]) = Sreg[k][half];
+                    if constexpr (kRegC)
+                        *reinterpret_cast<f32x4 *>(&BlkC[wave][32 * k + 8 * q4 + 4 * half]) = Kreg[k][half];
+                }
+            if (kRegC && q4 == 0) {
+                BlkG[wave] = Ac;
+                BlkB[wave] = Bq;
+            }
         }
     } else if constexpr (!QH) {
         float S[EPL], Ck[RM ? EPL : 1];
@@ -1073,26 +1145,52 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
 #pragma unroll
             for (int e = 0; e < EPL; ++e) C[e] = Cin[e];
         }
+        if constexpr (kRegC) {
+            // (S, C) through the earlier blocks: S = g_w·S + β_w·C + s_w, C += c_w
+            float K[EPL];
 #pragma unroll
-        for (int w = 0; w < 3; ++w) {
-            if (w < wave) {
-                const int s0 = t0 + kBlk * w;
-                const float gl = powi(gm, evict_steps(p0, s0, min(kBlk, n - s0), W));
+            for (int e = 0; e < EPL; ++e) K[e] = Kin[e];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) C[e] = gl * C[e] + BlkAgg[w][e0 + e];
+            for (int w = 0; w < 3; ++w) {
+                if (w < wave) {
+                    const float gw = BlkG[w], bw = BlkB[w];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        C[e] = gw * C[e] + bw * K[e] + BlkAgg[w][e0 + e];
+                        K[e] += BlkC[w][e0 + e];
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) Kb[wave][e0 + e] = K[e];
+        } else {
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                if (w < wave) {
+                    const int s0 = t0 + kBlk * w;
+                    const float gl = powi(gm, evict_steps(p0, s0, min(kBlk, n - s0), W));
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) C[e] = gl * C[e] + BlkAgg[w][e0 + e];
+                }
             }
         }
 #pragma unroll
         for (int e = 0; e < EPL; ++e) Sw[e0 + e] = C[e];
         wave_lds_sync();
-        // S_t = A_{..t}·S_start + V_{..t}
+        // S_t = A_{..t}·S_start + V_{..t} (running mean: + B_t·C_start)
 #pragma unroll
         for (int k = 0; k < D / 32; ++k)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&Sw[32 * k + 8 * q4 + 4 * half]);
+                if constexpr (kRegC) {
+                    const f32x4 k0 = *reinterpret_cast<const f32x4 *>(&Kb[wave][32 * k + 8 * q4 + 4 * half]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Sreg[k][half][i] = fmaf(Ac, s0[i], Sreg[k][half][i]);
+                    for (int i = 0; i < 4; ++i) Sreg[k][half][i] = fmaf(Ac, s0[i], fmaf(Bq, k0[i], Sreg[k][half][i]));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Sreg[k][half][i] = fmaf(Ac, s0[i], Sreg[k][half][i]);
+                }
             }
         if constexpr (FUSED || FOLD) {
             // the single pass and the folded form write S after the last token:

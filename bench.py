@@ -343,34 +343,43 @@ def run_variants(steps=10, warmup=2):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     res = {}
-    # prefill: layer 0 of the 64K workload, one decay per query head
-    d = inputs.workload(4, device=dev, layer=0)
-    gq = inputs.uniform((HQ,), 0.90, 0.99, 77, device=dev)
+    # prefill: three layers of the 64K workload in turn, so that no layer's
+    # K and V (134 MB) can stay in the 256 MB MALL from one call to its next
+    layers = [inputs.workload(4, device=dev, layer=i) for i in range(3)]
+
+    def prefill_ms(gammas, **kw):
+        # calls back to back, as the headline step runs its layers: events on
+        # the launch stream around all `reps` of them
+        reps = 3 * steps
+        for i in range(warmup):
+            d = layers[i % 3]
+            sfa.prefill(d["q"], d["k"], d["v"], gammas[i % 3], d["alpha"], **kw)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(reps):
+            d = layers[i % 3]
+            sfa.prefill(d["q"], d["k"], d["v"], gammas[i % 3], d["alpha"], **kw)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    # one decay per query head
+    gq = [inputs.uniform((HQ,), 0.90, 0.99, 77 + i, device=dev) for i in range(3)]
     kw = dict(window=WIN, out=torch.empty((B, N, HQ, HD), dtype=torch.bfloat16, device=dev),
               ring_k=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
               ring_v=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
               state=torch.zeros((B, HQ, HD), dtype=torch.float32, device=dev),
               workspace=torch.empty(sfa.prefill_workspace_size(B, N, HQ, HD), dtype=torch.uint8, device=dev),
               stream=stream, gamma_per_query_head=True)
-    for _ in range(warmup):
-        sfa.prefill(d["q"], d["k"], d["v"], gq, d["alpha"], **kw)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record(stream)
-        sfa.prefill(d["q"], d["k"], d["v"], gq, d["alpha"], **kw)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    ms = prefill_ms(gq, **kw)
     byts = prefill_bytes_per_launch() + B * HQ * HD * 4
     res["prefill_qh"] = {"workload": "7B-shaped 64K-token prefill layer, γ and S per query head",
                          "us_per_call": ms * 1e3, "value": B * N * HQ / (ms * 1e-3),
-                         "unit": "tokens·heads/s",
+                         "unit": "tokens·heads/s", "timing": "back-to-back calls over three layers in turn, events around all",
                          "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9,
                                       "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                       "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_call": byts}}
-    del d, kw
-    torch.cuda.empty_cache()
     # decode: the 28-layer step with S [L,B,Hq,d] and γ [L,Hq]
     L, Bd, Hq, Hkv, hd = 28, 256, 28, 4, 128
     sets = []
@@ -394,32 +403,22 @@ def run_variants(steps=10, warmup=2):
     del sets
     torch.cuda.empty_cache()
     # running mean of the keys that have left the window (state carries S and M)
-    d = inputs.workload(4, device=dev, layer=0)
-    kw = dict(window=WIN, out=torch.empty((B, N, HQ, HD), dtype=torch.bfloat16, device=dev),
+    kw = dict(window=WIN, out=kw["out"],
               ring_k=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
               ring_v=torch.zeros((B, HKV, WIN, HD), dtype=torch.bfloat16, device=dev),
               state=torch.zeros((B, HKV, 2, HD), dtype=torch.float32, device=dev),
               workspace=torch.empty(sfa.prefill_workspace_size(B, N, 3 * HKV, HD), dtype=torch.uint8,
                                     device=dev),
               stream=stream, running_mean=True)
-    for _ in range(warmup):
-        sfa.prefill(d["q"], d["k"], d["v"], d["gamma"], d["alpha"], **kw)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record(stream)
-        sfa.prefill(d["q"], d["k"], d["v"], d["gamma"], d["alpha"], **kw)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    ms = prefill_ms([d["gamma"] for d in layers], **kw)
     byts = prefill_bytes_per_launch() + B * HKV * HD * 4
     res["prefill_rm"] = {"workload": "7B-shaped 64K-token prefill layer, running mean of the keys that left the window",
                          "us_per_call": ms * 1e3, "value": B * N * HQ / (ms * 1e-3),
-                         "unit": "tokens·heads/s",
+                         "unit": "tokens·heads/s", "timing": "back-to-back calls over three layers in turn, events around all",
                          "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9,
                                       "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                                       "frac": byts / (ms * 1e-3) / PEAK_HBM, "bytes_per_call": byts}}
-    del d, kw
+    del layers, kw
     torch.cuda.empty_cache()
     sets = []
     for i in range(3):

@@ -9,9 +9,9 @@
 //
 // Three launches per call:
 //   k_ewma_agg    one wave per (b, KV head, 64-token tile): the tile's local
-//                 EWMA aggregate (scan from 0) and, where the attention kernel
-//                 reads them, its 16-token blocks' (fp32 inputs; with the
-//                 running mean, their key sums; with γ per query head, as
+//                 EWMA aggregate (scan from 0; with the running mean, its map
+//                 and key sum) and, where the attention kernel reads them, its
+//                 16-token blocks' (fp32 inputs; with γ per query head, as
 //                 block-start partials of every query head's chain).
 //   k_ewma_carry  one workgroup per (scan chain, 16 head-dim columns):
 //                 exclusive scan of the tile aggregates -> S just before every
@@ -83,7 +83,8 @@ __device__ __forceinline__ void load_epl(const T *p, float *x) {
 // incoming (S, C) to g·S + β·C + s and C + c, with g = γ^(evicting steps), c
 // the sum of the keys it evicts, s its S from (0, 0) and β = Σ over its
 // evicting steps of (1-γ)·γ^(later evicting steps)/m; m = p-W+1 at position p.
-// The kernel writes s and c per block and tile and β per tile.
+// The kernel writes s and c per tile (fp32 inputs: per block too) and β per
+// tile.
 // ---------------------------------------------------------------------------
 template <typename TIn, int D, bool RM, bool QH>
 __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
@@ -668,8 +669,9 @@ __device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float *v) {
 // QH: γ and S per query head (scan chains (b, query head)); each head's S tile
 // is rebuilt in the head loop from its carry and the wave's evicted keys.
 // RM: the running mean of the keys that have left the window is the EWMA
-// input; the wave starts from the tile's carried (S, C) and the block
-// aggregates of its earlier blocks, then scans C += k, S = γS + (1-γ)·C/m.
+// input; the wave starts from the tile's carried (S, C) and the maps of its
+// earlier blocks (bf16: formed by the waves' own row scans, shared through
+// LDS; fp32: written by k_ewma_agg), then scans C += k, S = γS + (1-γ)·C/m.
 // Two workgroups per CU, except fp32 inputs at d = 128: their fp32 K rows and
 // split V^T staging take 119 KB of LDS, so one workgroup per CU is all the
 // LDS allows and the register budget follows that.

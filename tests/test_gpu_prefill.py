@@ -61,6 +61,9 @@ SMALL = [  # (B, n, Hq, Hkv, hd, W)
     (1, 1, 1, 1, 64, 16), (2, 7, 3, 1, 64, 16), (1, 16, 2, 2, 128, 16), (1, 17, 7, 1, 128, 16),
     (2, 63, 4, 2, 64, 5), (1, 64, 7, 1, 128, 16), (3, 65, 6, 3, 64, 1), (1, 130, 14, 2, 64, 16),
     (2, 300, 8, 2, 128, 3), (1, 1000, 7, 1, 128, 16), (1, 200, 20, 1, 64, 16),
+    # more group sizes (3, 2, 8, 5, 1) on grids of a multiple of 8 tiles
+    (2, 256, 6, 2, 64, 16), (1, 512, 2, 1, 128, 16), (4, 100, 16, 2, 128, 16), (1, 500, 5, 1, 64, 7),
+    (8, 64, 1, 1, 64, 16),
 ]
 
 

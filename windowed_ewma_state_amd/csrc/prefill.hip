@@ -156,7 +156,9 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < kBlk; ++j) {
             if (!use[j]) continue;
-            const float inv_m = RM ? 1.f / (float)(p0 + tb + j - W + 1) : 0.f;
+            // 1/m by v_rcp_f32 (within 1 ulp; m >= 1 is exact in fp32), not the
+            // IEEE division sequence
+            const float inv_m = RM ? __builtin_amdgcn_rcpf((float)(p0 + tb + j - W + 1)) : 0.f;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 float v[EPC];
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     if constexpr (RM) {
         for (int j = 0; j < blen; ++j) {
             const int p = p0 + tb + j;
-            if (p >= W) bw = gm * bw + (1.f - gm) / (float)(p - W + 1);
+            if (p >= W) bw = gm * bw + (1.f - gm) * __builtin_amdgcn_rcpf((float)(p - W + 1));
         }
     }
     // (with bf16 inputs and S per KV head, plain or with the running mean, the
@@ -1009,7 +1011,7 @@ __global__ __launch_bounds__(256, (attn_wg_per_cu<TIn, D>())) void k_window_attn
             // S_t = Γ_t·S0 + B_t·C0 + V_t, where V_t = γ_t·V_{t-1} + β_t·K_t
             // and B_t = γ_t·B_{t-1} + β_t: a prefix sum, then the scan of
             // (γ_t, β_t·K_t) carrying B beside V.
-            const float bt = ev ? (1.f - gm) / (float)(p0 + t - W + 1) : 0.f;
+            const float bt = ev ? (1.f - gm) * __builtin_amdgcn_rcpf((float)(p0 + t - W + 1)) : 0.f;
             row_sum_step<1, D / 32>(Kreg);
             row_sum_step<2, D / 32>(Kreg);
             row_sum_step<4, D / 32>(Kreg);

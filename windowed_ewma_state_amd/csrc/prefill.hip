@@ -282,7 +282,7 @@ __device__ __forceinline__ int evict_steps(int p0, int s0, int len, int W) {
 
 // ---------------------------------------------------------------------------
 // k_ewma_carry: S before each tile (exclusive scan over tiles) and final S.
-// One workgroup per (b, KV head, 16 head-dim elements); 64 parts of the tile
+// One workgroup per (scan chain, 16 head-dim elements); 64 parts of the tile
 // range are scanned in parallel (up to kCarryRegs tiles per part: every load
 // of the part issued at once and kept in registers for the rescan), the part
 // aggregates are combined by one wave per column (a shuffle scan over the 64

@@ -21,6 +21,8 @@ def _prefill_inputs(B, n, Hq, Hkv, hd, seed, dtype=torch.bfloat16):
 PREFILL = [  # (B, n, Hq, Hkv, hd, W)
     (1, 1, 2, 1, 64, 16), (2, 63, 4, 2, 64, 5), (1, 130, 14, 2, 64, 16), (2, 300, 8, 2, 128, 3),
     (1, 1000, 7, 1, 128, 16), (3, 65, 6, 3, 64, 1),
+    # groups of 20 (more heads than the query slots and a 16-row MFMA tile), 1 and 5
+    (1, 200, 20, 1, 64, 16), (2, 150, 3, 3, 128, 16), (1, 257, 10, 2, 128, 7),
 ]
 
 

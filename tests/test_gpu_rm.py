@@ -14,6 +14,8 @@ pytestmark = pytest.mark.gpu
 PREFILL = [  # (B, n, Hq, Hkv, hd, W)
     (1, 1, 2, 1, 64, 16), (2, 63, 4, 2, 64, 5), (1, 130, 14, 2, 64, 16), (2, 300, 8, 2, 128, 3),
     (1, 1000, 7, 1, 128, 16), (3, 65, 6, 3, 64, 1), (1, 17, 4, 4, 128, 16),
+    # groups of 20, 1 and 5; positions from 1 to past 16 blocks
+    (1, 200, 20, 1, 64, 16), (2, 150, 3, 3, 128, 16), (1, 257, 10, 2, 128, 7),
 ]
 
 

@@ -115,6 +115,7 @@ def test_prefill_part_modes(kw, want):
     (dict(pos=None), INV), (dict(state=None), INV), (dict(ring_k=P + 8), INV),
     (dict(L=0, q=None), OK), (dict(B=0, pos=None), OK),
     (dict(L=1 << 13, B=1 << 12), INV),  # 64·L·B·Hkv reaches 2^31
+    (dict(L=1 << 12, B=1 << 11, Hq=2), INV),  # 128·L·B·Hq reaches 2^31 (64·L·B·Hkv is 2^29)
 ])
 def test_decode_rejects_before_launch(kw, want):
     assert _decode(**kw) == want

@@ -137,28 +137,50 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
             for (int e = lane; e < D; e += 64) c0p[e] = (a.pos0 && p0 > 0) ? a.state[bgs * D + e] : 0.f;
         }
     }
-    for (int jh = 0; jh < nh; ++jh) {
-    const int hs = QH ? G * a.group + jh : G;  // the scan chain's S head
-    const int bg = b * a.Hs + hs;
-    const float gm = a.gamma[hs];
-    float A[CPL][EPC], Cs[RM ? CPL : 1][EPC];
+    // γ per query head: the keys are converted once per pass and folded into
+    // HC chains at a time (heads past the group repeat the last one)
+    constexpr int HC = QH ? 2 : 1;
+    const int blen = max(0, min(kBlk, n - tb));
+    const int steps = max(0, blen - max(0, W - p0 - tb));
+    for (int h0 = 0; h0 < nh; h0 += HC) {
+    float gmh[HC];
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
+    for (int hh = 0; hh < HC; ++hh) gmh[hh] = a.gamma[QH ? G * a.group + min(h0 + hh, nh - 1) : G];
+    float Ah[HC][CPL][EPC], Cs[RM ? CPL : 1][EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) A[cc][e] = 0.f;
+    for (int hh = 0; hh < HC; ++hh)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) Ah[hh][cc][e] = 0.f;
+    // RM: the block folds the running means C_j/m_j of its evicting tokens,
+    // Σ_j γ^(evicting tokens after j)·C_j/m_j = Σ_i k_i·w_i with
+    // w_i = Σ_{j >= i} γ^(evicting tokens after j)/m_j (a suffix sum, the same
+    // for every lane of the block); w at the first evicting token is β/(1-γ).
+    // 1/m by v_rcp_f32 (within 1 ulp; m >= 1 is exact in fp32), not the IEEE
+    // division sequence.
+    float wt[RM ? kBlk : 1];
+    float wsum = 0.f;
     if constexpr (RM) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
             for (int e = 0; e < EPC; ++e) Cs[cc][e] = 0.f;
+        float gp = 1.f;
+#pragma unroll
+        for (int j = kBlk - 1; j >= 0; --j) {
+            const int p = p0 + tb + j;
+            if (tb + j < n && p >= W) {
+                wsum = fmaf(gp, __builtin_amdgcn_rcpf((float)(p - W + 1)), wsum);
+                gp *= gmh[0];
+            }
+            wt[j] = wsum;
+        }
     }
     if (lane_ok) {
 #pragma unroll
         for (int j = 0; j < kBlk; ++j) {
             if (!use[j]) continue;
-            // 1/m by v_rcp_f32 (within 1 ulp; m >= 1 is exact in fp32), not the
-            // IEEE division sequence
-            const float inv_m = RM ? __builtin_amdgcn_rcpf((float)(p0 + tb + j - W + 1)) : 0.f;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 float v[EPC];
@@ -177,33 +199,36 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
 #pragma unroll
                     for (int e = 0; e < EPC; ++e) {
                         Cs[cc][e] += v[e];
-                        A[cc][e] = fmaf(gm, A[cc][e], Cs[cc][e] * inv_m);
+                        Ah[0][cc][e] = fmaf(wt[j], v[e], Ah[0][cc][e]);
                     }
                 } else {
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) A[cc][e] = fmaf(gm, A[cc][e], v[e]);
+                    for (int hh = 0; hh < HC; ++hh)
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) Ah[hh][cc][e] = fmaf(gmh[hh], Ah[hh][cc][e], v[e]);
                 }
             }
         }
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
+        for (int hh = 0; hh < HC; ++hh)
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) A[cc][e] *= 1.f - gm;
+            for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) Ah[hh][cc][e] *= 1.f - gmh[hh];
     }
+#pragma unroll
+    for (int hh = 0; hh < HC; ++hh) {
+    if (h0 + hh >= nh) break;
+    const int hs = QH ? G * a.group + h0 + hh : G;  // the scan chain's S head
+    const int bg = b * a.Hs + hs;
+    const float gm = gmh[hh];
+    float (&A)[CPL][EPC] = Ah[hh];
     // 16-token block aggregates, then the tile aggregate: blocks combined in
     // order through LDS, T = ((A0·g1 + A1)·g2 + A2)·g3 + A3 with g_w the decay
     // over block w's evicting steps (RM: T = g_w·T + β_w·TC + A_w, TC += C_w)
     float *a16 = a.agg16 + (((long)bg * a.ntiles + tile) * 4 + blk) * D;
-    const int blen = max(0, min(kBlk, n - tb));
-    const int steps = max(0, blen - max(0, W - p0 - tb));
     const float gl = powi(gm, steps);
-    float bw = 0.f;  // RM: β of this lane's block
-    if constexpr (RM) {
-        for (int j = 0; j < blen; ++j) {
-            const int p = p0 + tb + j;
-            if (p >= W) bw = gm * bw + (1.f - gm) * __builtin_amdgcn_rcpf((float)(p - W + 1));
-        }
-    }
+    const float bw = RM ? (1.f - gm) * wsum : 0.f;  // RM: β of this lane's block
     // (with bf16 inputs and S per KV head, plain or with the running mean, the
     // attention kernel forms the block maps from its own scan and reads only
     // the tile carries; with γ per query head the tile composition below
@@ -271,6 +296,7 @@ __global__ __launch_bounds__(256) void k_ewma_agg(PrefillArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     }
 }
 

@@ -87,6 +87,8 @@ DECODE = [  # (L, B, Hq, Hkv, hd, W, in_dtype)
     (1, 5, 4, 4, 128, 4, torch.bfloat16),
     (3, 5, 6, 1, 64, 1, torch.bfloat16),
     (2, 5, 36, 2, 128, 16, torch.bfloat16),  # 18 query heads per KV head: the VALU kernel
+    (2, 5, 24, 2, 128, 16, torch.bfloat16),  # 12 query heads per KV head: 16-row query tiles (d 128)
+    (2, 5, 32, 2, 64, 16, torch.bfloat16),  # 16 query heads per KV head: 16-row query tiles (d 64)
     (2, 5, 8, 2, 128, 16, torch.float32),
     (1, 5, 3, 3, 64, 7, torch.float32),
 ]
